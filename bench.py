@@ -1,0 +1,230 @@
+"""Benchmark of the shard-local update on one MI355X.
+
+A step is one call of zero_shard_step over one rank's whole shard: the
+rank-ordered reduction of the N_d bf16 contributions, AdamW on the fp32
+master / m / v shard, and the bf16 store into the rank's All-Gather slots (or
+in place for ZeRO-3).  Inputs are seeded synthetic data generated on the GPU
+before the timed region and stay resident in HBM; the optimizer state evolves
+across the timed steps (t increases), the contributions are reused.
+
+Default workload: the Llama-3-8B parameter list (8,030,261,248 parameters)
+in 25 MiB buckets at N_d = 8, rank 7: a 1,003,782,656-element shard, eight
+bf16 contributions (16 GB), 42 bytes per shard element.
+
+Prints one JSON line (rank 0).  `value` is shard elements updated per second;
+`roofline` is the step kernel's algorithmic HBM bytes per launch over its
+average launch duration (HIP events on the launch stream); `cpu_baseline` is
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+KERNEL_SOURCES = ["fsdp_sharded_optimizer_step_amd/csrc/shard_step.hip",
+                  "fsdp_sharded_optimizer_step_amd/csrc/device_common.hpp"]
+
+WORKLOAD_LABEL = {
+    "llama8b": "Llama-3-8B shard: 8.03e9 params, 25 MiB buckets, N_d=8, rank 7, ZeRO-1/2 AG slot",
+    "llama70b": "Llama-70B shard: 7.06e10 params, 25 MiB buckets, N_d=64, rank 63, ZeRO-3 in place",
+    "llama70b_t": "Llama-70B shard: 12.5e6-element buckets (padded tails), N_d=64, rank 63, ZeRO-3",
+}
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, n_launch_bytes: float):
+    """Measured HBM bytes per launch from the committed counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"shard_step_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_hash") != kernel_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def build_inputs(z, synth, w, L):
+    import torch
+    dev = torch.device("cuda:0")
+    buckets = L.buckets()
+    so, ln, po, pl, sh = (list(x) for x in zip(*buckets))
+    segs = synth.shard_segments(so, ln, pl, sh, w.n_d, w.rank)
+    S, P = L.shard, L.padded
+    grads = []
+    for q in range(w.n_d):
+        g = torch.empty(S, dtype=torch.int16, device=dev)
+        synth.fill_device(g, segs, synth.key(w.name, "grad", q, 0, w.t_first), *w.grad)
+        grads.append(g)
+    state = []
+    for kind, dist in (("master", w.master), ("exp_avg", w.exp_avg),
+                       ("exp_avg_sq", w.exp_avg_sq)):
+        b = torch.empty(S, dtype=torch.float32, device=dev)
+        synth.fill_device(b, segs, synth.key(w.name, kind), *dist)
+        state.append(b)
+    pout = torch.zeros(P if w.out_mode == "ag_slot" else S, dtype=torch.int16, device=dev)
+    torch.cuda.synchronize()
+    return grads, state, pout, segs
+
+
+def cpu_baseline(w, segs, S, target_s=12.0):
+    """The CPU oracle on a contiguous sample of the shard (inputs generated
+    outside the timed region), all host threads up to 16."""
+    import numpy as np
+
+    import oracle
+    import synth
+    threads = max(1, min(16, os.cpu_count() or 1))
+
+    def sample_inputs(n):
+        sub, left = [], n
+        for d, x0, nr, npd in segs:
+            if left <= 0:
+                break
+            take_r = min(nr, left)
+            take_p = min(npd, left - take_r)
+            sub.append((d if not sub else sum(s[2] + s[3] for s in sub), x0, take_r, take_p))
+            left -= take_r + take_p
+        n = sum(s[2] + s[3] for s in sub)
+        G = [synth.fill_host(n, synth.OUT_BF16, sub,
+                             synth.key(w.name, "grad", q, 0, w.t_first), *w.grad)
+             for q in range(w.n_d)]
+        st = [synth.fill_host(n, synth.OUT_F32, sub, synth.key(w.name, k), *dist)
+              for k, dist in (("master", w.master), ("exp_avg", w.exp_avg),
+                              ("exp_avg_sq", w.exp_avg_sq))]
+        return n, G, st
+
+    hp = oracle.AdamW(**w.hp)
+    n, G, st = sample_inputs(min(S, 1 << 20))
+    t0 = time.perf_counter()
+    oracle.shard_step(G, *st, hp, w.t_first, nthreads=threads)
+    pilot = max(1e-6, time.perf_counter() - t0)
+    rate = n / pilot
+    n_target = int(min(S, max(n, rate * target_s), 96 << 20))
+    n, G, st = sample_inputs(n_target)
+    t0 = time.perf_counter()
+    oracle.shard_step(G, *st, hp, w.t_first, nthreads=threads)
+    dt = time.perf_counter() - t0
+    del G, st
+    return {"value": n / dt, "unit": "elem/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} elements of the same shard (inputs generated untimed), "
+                      f"one step, {dt:.1f} s on {threads} host threads",
+            "gbps": n * (2 * w.n_d + 26) / dt / 1e9}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b", choices=sorted(WORKLOAD_LABEL))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--blocks", type=int, default=0)
+    ap.add_argument("--threads", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the shard step of one rank); "
+              "--gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fsdp_sharded_optimizer_step_amd as z
+    import synth
+    from synth import workloads
+
+    z.load()
+    w = workloads.get(args.workload)
+    L = z.Layout(w.numel, w.cap, w.n_d, w.rank)
+    S, P = L.shard, L.padded
+    print(f"# workload {w.name}: S={S} P={P} N_d={w.n_d} buckets={L.n_buckets}", file=sys.stderr,
+          flush=True)
+    grads, (master, m, v), pout, segs = build_inputs(z, synth, w, L)
+    hp = z.AdamW(**w.hp)
+    gl = z.GRAD_COMPACT if w.grad_layout == "compact" else z.GRAD_FLAT
+    om = z.OUT_AG_SLOT if w.out_mode == "ag_slot" else z.OUT_SHARD
+    launch = (args.blocks, args.threads, 0) if (args.blocks or args.threads) else None
+    stream = torch.cuda.current_stream()
+
+    def step(t):
+        z.zero_shard_step(L, hp, t, grads, gl, master, m, v, pout, om, launch=launch,
+                          stream=stream)
+
+    t = w.t_first
+    for _ in range(args.warmup):
+        step(t)
+        t += 1
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        step(t)
+        ev[k][1].record(stream)
+        t += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    k_avg = sum(kernel_ms) / len(kernel_ms)
+    bytes_per_elem = 2 * w.n_d + 26
+    alg_bytes = S * bytes_per_elem
+    achieved = alg_bytes / (k_avg * 1e-3) / 1e9
+    traffic = traffic_from_profiles(w.name, alg_bytes)
+    print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, kernel avg {k_avg:.3f} ms "
+          f"(min {min(kernel_ms):.3f}, max {max(kernel_ms):.3f}); {achieved:.0f} GB/s",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        del grads
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(w, segs, S)
+    out = {
+        "metric": "shard-step elements/s and achieved HBM GB/s (% of MI355X peak), 1 GPU",
+        "value": S / (ms_per_step * 1e-3),
+        "unit": "elem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded counter-based generator, resident in HBM)",
+        "hbm_GBps": alg_bytes / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac_of_peak": alg_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "config": {"workload": w.name, "description": WORKLOAD_LABEL[w.name], "shard_elems": S,
+                   "padded_elems": P, "n_d": w.n_d, "rank": w.rank, "buckets": L.n_buckets,
+                   "grad_layout": w.grad_layout, "out_mode": w.out_mode,
+                   "bytes_per_elem": bytes_per_elem, "io": "bf16 grads and params, f32 state"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "kernel": "step_vec_kernel", "kernel_avg_ms": k_avg,
+                     "algorithmic_bytes_per_launch": alg_bytes, "kernel_hash": kernel_hash()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

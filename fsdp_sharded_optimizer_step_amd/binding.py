@@ -1,0 +1,224 @@
+"""Thin Python binding of libzero_shard.so (the C ABI in include/zero_shard.h).
+
+Argument marshalling only: torch CUDA tensors supply device pointers and the
+current HIP stream; every step of the update runs in the library's kernels.
+bf16 buffers may be torch.bfloat16, torch.int16 or torch.uint16 tensors (the
+library reads and writes 16-bit patterns).  Failing to find the built library
+raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzero_shard.so")
+
+ZERO_OK, ZERO_EINVAL, ZERO_ERANGE, ZERO_EHIP, ZERO_EOVERLAP = 0, -1, -3, -4, -5
+ZERO_MAX_ND = 256
+GRAD_COMPACT, GRAD_FLAT = 0, 1
+OUT_AG_SLOT, OUT_SHARD = 0, 1
+ACC_OVERWRITE, ACC_EMIT_BF16, ACC_NO_STORE = 1, 2, 4
+
+EXPORTS = ("zero_layout_create", "zero_layout_destroy", "zero_layout_psi", "zero_layout_padded",
+           "zero_layout_shard", "zero_layout_n_buckets", "zero_layout_n_d", "zero_layout_rank",
+           "zero_layout_bucket", "zero_layout_tensor", "zero_bucket_pack", "zero_grad_accumulate",
+           "zero_shard_step", "zero_shard_step_ex", "zero_step_scalars", "zero_strerror")
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, where: str, status: int):
+        super().__init__(f"{where}: {_lib_strerror(status)} (status {status})")
+        self.status = status
+
+
+class _AdamW(C.Structure):
+    _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
+                ("eps", C.c_double), ("weight_decay", C.c_double)]
+
+
+class _Launch(C.Structure):
+    _fields_ = [("blocks", C.c_int32), ("threads", C.c_int32), ("path", C.c_int32)]
+
+
+_lib = None
+_i64p = C.POINTER(C.c_int64)
+
+
+def load():
+    """Load the built library (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(no fallback path exists)")
+    lib = C.CDLL(LIB_PATH)
+    vp = C.c_void_p
+    lib.zero_layout_create.argtypes = [_i64p, C.c_int32, C.c_int64, C.c_int32, C.c_int32,
+                                       C.POINTER(vp)]
+    lib.zero_layout_destroy.argtypes = [vp]
+    lib.zero_layout_destroy.restype = None
+    for name in ("zero_layout_psi", "zero_layout_padded", "zero_layout_shard",
+                 "zero_layout_n_buckets"):
+        getattr(lib, name).argtypes = [vp]
+        getattr(lib, name).restype = C.c_int64
+    for name in ("zero_layout_n_d", "zero_layout_rank"):
+        getattr(lib, name).argtypes = [vp]
+        getattr(lib, name).restype = C.c_int32
+    lib.zero_layout_bucket.argtypes = [vp, C.c_int64] + [_i64p] * 5
+    lib.zero_layout_tensor.argtypes = [vp, C.c_int32] + [_i64p] * 3
+    lib.zero_bucket_pack.argtypes = [vp, C.POINTER(vp), C.c_int64, C.c_int64, vp, vp]
+    lib.zero_grad_accumulate.argtypes = [vp, vp, C.c_int64, C.c_float, C.c_uint32, vp, vp]
+    lib.zero_shard_step.argtypes = [vp, C.POINTER(_AdamW), C.c_int64, C.POINTER(vp), C.c_int32,
+                                    vp, vp, vp, vp, C.c_int32, vp, vp]
+    lib.zero_shard_step_ex.argtypes = [vp, C.POINTER(_AdamW), C.c_int64, C.POINTER(vp),
+                                       C.c_int32, vp, vp, vp, vp, C.c_int32, vp,
+                                       C.POINTER(_Launch), vp]
+    lib.zero_step_scalars.argtypes = [C.POINTER(_AdamW), C.c_int64, C.POINTER(C.c_float)]
+    lib.zero_strerror.argtypes = [C.c_int]
+    lib.zero_strerror.restype = C.c_char_p
+    _lib = lib
+    return lib
+
+
+def _lib_strerror(status: int) -> str:
+    try:
+        return load().zero_strerror(status).decode()
+    except Exception:  # pragma: no cover - only used for messages
+        return "error"
+
+
+def _check(where: str, rc: int):
+    if rc != ZERO_OK:
+        raise ZeroError(where, rc)
+
+
+@dataclass
+class AdamW:
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.95
+    eps: float = 1e-8
+    weight_decay: float = 0.1
+
+    def _c(self):
+        return _AdamW(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay)
+
+
+class Layout:
+    """Owning wrapper of a zero_layout (host object)."""
+
+    def __init__(self, numel, bucket_cap: int, n_d: int, rank: int):
+        lib = load()
+        arr = (C.c_int64 * max(1, len(numel)))(*[int(n) for n in numel])
+        h = C.c_void_p()
+        _check("zero_layout_create", lib.zero_layout_create(arr, len(numel), int(bucket_cap),
+                                                            int(n_d), int(rank), C.byref(h)))
+        self._h = h
+        self.n_tensors = len(numel)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.zero_layout_destroy(h)
+            self._h = None
+
+    psi = property(lambda self: load().zero_layout_psi(self._h))
+    padded = property(lambda self: load().zero_layout_padded(self._h))
+    shard = property(lambda self: load().zero_layout_shard(self._h))
+    n_buckets = property(lambda self: load().zero_layout_n_buckets(self._h))
+    n_d = property(lambda self: load().zero_layout_n_d(self._h))
+    rank = property(lambda self: load().zero_layout_rank(self._h))
+
+    def bucket(self, b: int):
+        """-> (stream_off, len, padded_off, padded_len, shard_off)"""
+        vals = [C.c_int64() for _ in range(5)]
+        _check("zero_layout_bucket", load().zero_layout_bucket(self._h, b, *[C.byref(v) for v in vals]))
+        return tuple(v.value for v in vals)
+
+    def buckets(self):
+        return [self.bucket(b) for b in range(self.n_buckets)]
+
+    def tensor(self, t: int):
+        """-> (stream_off, shard_lo, shard_hi)"""
+        vals = [C.c_int64() for _ in range(3)]
+        _check("zero_layout_tensor", load().zero_layout_tensor(self._h, t, *[C.byref(v) for v in vals]))
+        return tuple(v.value for v in vals)
+
+
+def _stream_ptr(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dev16(t, name):
+    if t is None:
+        return None
+    if not (t.is_cuda and t.is_contiguous() and t.element_size() == 2):
+        raise ValueError(f"{name}: needs a contiguous 16-bit CUDA tensor")
+    return C.c_void_p(t.data_ptr())
+
+
+def _dev32(t, name):
+    import torch
+    if t is None:
+        return None
+    if not (t.is_cuda and t.is_contiguous() and t.dtype == torch.float32):
+        raise ValueError(f"{name}: needs a contiguous float32 CUDA tensor")
+    return C.c_void_p(t.data_ptr())
+
+
+def _ptr_array(tensors, name):
+    arr = (C.c_void_p * max(1, len(tensors)))()
+    for k, t in enumerate(tensors):
+        arr[k] = None if t is None else _dev16(t, f"{name}[{k}]").value
+    return arr
+
+
+def zero_bucket_pack(layout: Layout, tensor_grads, flat_out, bucket_begin: int = 0,
+                     bucket_end: int | None = None, stream=None):
+    if len(tensor_grads) != layout.n_tensors:
+        raise ValueError("zero_bucket_pack: one pointer per tensor is required")
+    end = layout.n_buckets if bucket_end is None else bucket_end
+    _check("zero_bucket_pack", load().zero_bucket_pack(
+        layout.handle, _ptr_array(tensor_grads, "tensor_grads"), bucket_begin, end,
+        _dev16(flat_out, "flat_out"), _stream_ptr(stream)))
+
+
+def zero_grad_accumulate(acc, grad, scale: float, flags: int = 0, bf16_out=None, n=None,
+                         stream=None):
+    n = grad.numel() if n is None else n
+    _check("zero_grad_accumulate", load().zero_grad_accumulate(
+        _dev32(acc, "acc"), _dev16(grad, "grad"), n, scale, flags, _dev16(bf16_out, "bf16_out"),
+        _stream_ptr(stream)))
+
+
+def zero_shard_step(layout: Layout, hp: AdamW, t: int, rank_grads, grad_layout: int, master,
+                    exp_avg, exp_avg_sq, param_out, out_mode: int, reduced_grad_out=None,
+                    stream=None, launch=None):
+    """One shard step; `launch` = (blocks, threads, path) selects the launch
+    shape (zero_shard_step_ex)."""
+    if len(rank_grads) != layout.n_d:
+        raise ValueError("zero_shard_step: one contribution per rank is required")
+    args = [layout.handle, C.byref(hp._c()), int(t), _ptr_array(rank_grads, "rank_grads"),
+            grad_layout, _dev32(master, "master"), _dev32(exp_avg, "exp_avg"),
+            _dev32(exp_avg_sq, "exp_avg_sq"), _dev16(param_out, "param_out"), out_mode,
+            _dev32(reduced_grad_out, "reduced_grad_out")]
+    if launch is None:
+        _check("zero_shard_step", load().zero_shard_step(*args, _stream_ptr(stream)))
+    else:
+        _check("zero_shard_step_ex", load().zero_shard_step_ex(
+            *args, C.byref(_Launch(*launch)), _stream_ptr(stream)))
+
+
+def zero_step_scalars(hp: AdamW, t: int):
+    out = (C.c_float * 8)()
+    _check("zero_step_scalars", load().zero_step_scalars(C.byref(hp._c()), t, out))
+    return list(out)

@@ -1,0 +1,218 @@
+// zero_bucket_pack and zero_grad_accumulate.
+//
+// Page "Infra: Data Parallel" (pufanyi.com), section "Naive Data
+// Parallelism": gradients of several parameters share one bucket that is
+// communicated once all of them are ready; with gradient accumulation the
+// micro-batch gradients are summed locally (no_sync) and each micro-batch
+// loss is divided by the number of micro-batches.  Section "FSDP1": the
+// parameters of a unit are flattened and concatenated into one flat buffer
+// that is split evenly, padding included.
+//
+// Both kernels are HBM streams: 128-bit loads/stores, grid-stride loops, no
+// LDS.  Pack moves 4 bytes per element (2 per pad element); accumulate moves
+// 6 (overwrite), 10 (add) or 8 (add, emit bf16, no fp32 store) bytes.
+#include <algorithm>
+#include <cstdint>
+#include <vector>
+
+#include "device_common.hpp"
+#include "layout.hpp"
+#include "zero_shard.h"
+
+namespace {
+using namespace zs;
+
+// ------------------------------------------------------------------ pack
+struct Piece {
+  const uint16_t* src;  // nullptr: write zeros (bucket padding)
+  int64_t dst;          // element offset in the flat buffer
+  int64_t n;            // element count
+};
+constexpr int kPiecesPerLaunch = 64;
+struct PackArgs {
+  Piece p[kPiecesPerLaunch];
+  uint16_t* out;
+};
+
+__global__ void __launch_bounds__(256) pack_kernel(const PackArgs A) {
+  const Piece pc = A.p[blockIdx.y];
+  uint16_t* d = A.out + pc.dst;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t T = (int64_t)gridDim.x * blockDim.x;
+  const uintptr_t da = (uintptr_t)d;
+  const bool zeros = pc.src == nullptr;
+  const bool vec = zeros || (((da ^ (uintptr_t)pc.src) & 15u) == 0);
+  if (!vec) {
+    for (int64_t e = tid; e < pc.n; e += T) d[e] = pc.src[e];
+    return;
+  }
+  // peel to 16-byte alignment of the destination (same phase as the source)
+  const int64_t head = std::min<int64_t>(pc.n, (int64_t)(((16u - (da & 15u)) & 15u) >> 1));
+  const int64_t nv = (pc.n - head) >> 3;
+  const int64_t tail0 = head + (nv << 3);
+  if (tid < head) d[tid] = zeros ? (uint16_t)0 : pc.src[tid];
+  if (tid < pc.n - tail0) d[tail0 + tid] = zeros ? (uint16_t)0 : pc.src[tail0 + tid];
+  u32x4* dv = (u32x4*)(d + head);
+  if (zeros) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int64_t k = tid; k < nv; k += T) st_stream(dv + k, z);
+  } else {
+    const u32x4* sv = (const u32x4*)(pc.src + head);
+    for (int64_t k = tid; k < nv; k += T) st_stream(dv + k, ld_stream(sv + k));
+  }
+}
+
+// ------------------------------------------------------------------ accumulate
+__global__ void __launch_bounds__(256) accum_vec_kernel(float* acc, const uint16_t* g, int64_t n,
+                                                        float scale, uint32_t flags,
+                                                        uint16_t* out) {
+  const bool overwrite = flags & ZERO_ACC_OVERWRITE;
+  const bool emit = flags & ZERO_ACC_EMIT_BF16;
+  const bool store = !(flags & ZERO_ACC_NO_STORE);
+  const int64_t nv = n >> 3;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t T = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t k = tid; k < nv; k += T) {
+    const int64_t i = k << 3;
+    const u32x4 w = ld_stream((const u32x4*)(g + i));
+    float a[8] = {scale * bf16_lo(w.x), scale * bf16_hi(w.x), scale * bf16_lo(w.y),
+                  scale * bf16_hi(w.y), scale * bf16_lo(w.z), scale * bf16_hi(w.z),
+                  scale * bf16_lo(w.w), scale * bf16_hi(w.w)};
+    if (!overwrite) {
+      const f32x4 a0 = ld_stream((const f32x4*)(acc + i));
+      const f32x4 a1 = ld_stream((const f32x4*)(acc + i + 4));
+      a[0] = a0.x + a[0]; a[1] = a0.y + a[1]; a[2] = a0.z + a[2]; a[3] = a0.w + a[3];
+      a[4] = a1.x + a[4]; a[5] = a1.y + a[5]; a[6] = a1.z + a[6]; a[7] = a1.w + a[7];
+    }
+    if (store) {
+      st_stream((f32x4*)(acc + i), f32x4{a[0], a[1], a[2], a[3]});
+      st_stream((f32x4*)(acc + i + 4), f32x4{a[4], a[5], a[6], a[7]});
+    }
+    if (emit)
+      st_stream((u32x4*)(out + i), u32x4{bf16_pack2(a[0], a[1]), bf16_pack2(a[2], a[3]),
+                                         bf16_pack2(a[4], a[5]), bf16_pack2(a[6], a[7])});
+  }
+  const int64_t tail0 = nv << 3;
+  if (tid < n - tail0) {
+    const int64_t i = tail0 + tid;
+    const float c = scale * bf16_one(g[i]);
+    const float a = overwrite ? c : acc[i] + c;
+    if (store) acc[i] = a;
+    if (emit) out[i] = (uint16_t)bf16_round(a);
+  }
+}
+
+__global__ void __launch_bounds__(256) accum_scalar_kernel(float* acc, const uint16_t* g,
+                                                           int64_t n, float scale, uint32_t flags,
+                                                           uint16_t* out) {
+  const bool overwrite = flags & ZERO_ACC_OVERWRITE;
+  const bool emit = flags & ZERO_ACC_EMIT_BF16;
+  const bool store = !(flags & ZERO_ACC_NO_STORE);
+  const int64_t T = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += T) {
+    const float c = scale * bf16_one(g[i]);
+    const float a = overwrite ? c : acc[i] + c;
+    if (store) acc[i] = a;
+    if (emit) out[i] = (uint16_t)bf16_round(a);
+  }
+}
+
+int cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+bool a16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+int zero_bucket_pack(const zero_layout* L, const uint16_t* const* tensor_grads,
+                     int64_t bucket_begin, int64_t bucket_end, uint16_t* flat_out,
+                     hipStream_t stream) {
+  if (!L || !flat_out) return ZERO_EINVAL;
+  if (bucket_begin < 0 || bucket_end > L->nb || bucket_begin > bucket_end) return ZERO_ERANGE;
+  const int32_t nt = (int32_t)L->numel.size();
+  if (nt > 0 && !tensor_grads) return ZERO_EINVAL;
+  // pieces: (tensor part inside bucket) and (bucket padding)
+  std::vector<Piece> pieces;
+  int32_t t = 0;
+  for (int64_t b = bucket_begin; b < bucket_end; ++b) {
+    const int64_t x0 = L->bucket_stream_off(b), x1 = x0 + L->bucket_len(b);
+    const int64_t base = L->bucket_padded_off(b);
+    // first tensor whose range ends after x0
+    t = (int32_t)(std::upper_bound(L->tensor_off.begin(), L->tensor_off.end(), x0) -
+                  L->tensor_off.begin()) - 1;
+    if (t < 0) t = 0;
+    for (; t < nt && L->tensor_off[t] < x1; ++t) {
+      const int64_t a = std::max(x0, L->tensor_off[t]);
+      const int64_t z = std::min(x1, L->tensor_off[t] + L->numel[t]);
+      if (a >= z) continue;
+      const uint16_t* src = tensor_grads[t];
+      if (!src) return ZERO_EINVAL;
+      pieces.push_back(Piece{src + (a - L->tensor_off[t]), base + (a - x0), z - a});
+    }
+    const int64_t pad = L->bucket_padded(b) - L->bucket_len(b);
+    if (pad > 0) pieces.push_back(Piece{nullptr, base + L->bucket_len(b), pad});
+  }
+  // sources must not overlap the destination
+  for (int32_t k = 0; k < nt; ++k)
+    if (tensor_grads[k] && overlap(tensor_grads[k], 2 * L->numel[k], flat_out, 2 * L->P))
+      return ZERO_EOVERLAP;
+  if (pieces.empty()) return ZERO_OK;
+  const int64_t cap = (int64_t)cus() * 8;
+  for (size_t p0 = 0; p0 < pieces.size(); p0 += kPiecesPerLaunch) {
+    PackArgs A;
+    A.out = flat_out;
+    const int cnt = (int)std::min<size_t>(kPiecesPerLaunch, pieces.size() - p0);
+    int64_t maxn = 1;
+    for (int k = 0; k < cnt; ++k) {
+      A.p[k] = pieces[p0 + k];
+      maxn = std::max(maxn, A.p[k].n);
+    }
+    const int64_t work = (maxn + 7) / 8 + 8;
+    const int gx = (int)std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256,
+                                                               std::max<int64_t>(1, cap / cnt)));
+    hipLaunchKernelGGL(pack_kernel, dim3(gx, cnt), dim3(256), 0, stream, A);
+    if (hipGetLastError() != hipSuccess) return ZERO_EHIP;
+  }
+  return ZERO_OK;
+}
+
+int zero_grad_accumulate(float* acc, const uint16_t* grad, int64_t n, float scale, uint32_t flags,
+                         uint16_t* bf16_out, hipStream_t stream) {
+  if (n < 0 || (flags & ~(ZERO_ACC_OVERWRITE | ZERO_ACC_EMIT_BF16 | ZERO_ACC_NO_STORE)))
+    return ZERO_EINVAL;
+  const bool overwrite = flags & ZERO_ACC_OVERWRITE;
+  const bool emit = flags & ZERO_ACC_EMIT_BF16;
+  const bool store = !(flags & ZERO_ACC_NO_STORE);
+  if (!store && !emit) return ZERO_EINVAL;
+  if (n == 0) return ZERO_OK;
+  if (!grad || (emit && !bf16_out) || ((store || !overwrite) && !acc)) return ZERO_EINVAL;
+  if (overlap(grad, 2 * n, acc, 4 * n) || (emit && (overlap(bf16_out, 2 * n, grad, 2 * n) ||
+                                                   overlap(bf16_out, 2 * n, acc, 4 * n))))
+    return ZERO_EOVERLAP;
+  const int64_t cap = (int64_t)cus() * 8;
+  const bool vec = a16(grad) && (!acc || a16(acc)) && (!emit || a16(bf16_out));
+  const int64_t work = vec ? std::max<int64_t>(n >> 3, 8) : n;
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256, cap));
+  if (vec)
+    hipLaunchKernelGGL(accum_vec_kernel, dim3(blocks), dim3(256), 0, stream, acc, grad, n, scale,
+                       flags, bf16_out);
+  else
+    hipLaunchKernelGGL(accum_scalar_kernel, dim3(blocks), dim3(256), 0, stream, acc, grad, n,
+                       scale, flags, bf16_out);
+  return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,224 @@
+/*
+ * zero_shard.h -- C ABI of the ZeRO / FSDP shard-local update for gfx950.
+ *
+ * What the library computes (page "Infra: Data Parallel", pufanyi.com):
+ *   - section "Zero Redundancy Optimizer (ZeRO)": AdamW updates each element
+ *     independently, so after a Reduce-Scatter with averaging hands every
+ *     rank the mean gradient of its own slice, the rank updates only its
+ *     slice of the parameters and of the fp32 optimizer state (master
+ *     weights, first and second moments: k = 12 bytes per parameter), and an
+ *     All-Gather (ZeRO-1/2) redistributes the updated 16-bit parameters;
+ *     under ZeRO-3 the rank keeps its updated shard and gathers nothing.
+ *   - section "Naive Data Parallelism": gradients of many parameters travel
+ *     together in a bucket; with gradient accumulation (no_sync) the
+ *     micro-batch gradients are summed locally, each scaled by 1/n_micro.
+ *   - section "Fully Sharded Data Parallel (FSDP)", "FSDP1": parameters are
+ *     flattened, concatenated and split evenly over the ranks; a split may
+ *     cut a tensor, and a rank may hold none of a tensor.
+ *
+ * On one GPU, the N_d ranks' gradient contributions are N_d device buffers;
+ * the library performs the local arithmetic of the Reduce-Scatter (a sum in
+ * fixed rank order, then the division by N_d), the optimizer step and the
+ * local write of the All-Gather (the rank's bf16 slice into its slot of the
+ * gathered buffer), in one kernel per call.  No collective is issued.
+ *
+ * Conventions for every entry point:
+ *   - Returns ZERO_OK or a negative zero_status.  Arguments are validated on
+ *     the host before anything is launched; on error nothing is launched and
+ *     no memory is touched.
+ *   - Pointers named *_dev are device pointers; everything else is host.
+ *     The caller owns all memory.  The library allocates no device memory.
+ *   - Work is enqueued on `stream` (NULL = the null stream) and is
+ *     asynchronous; results are visible after the caller synchronises.
+ *     A failed launch returns ZERO_EHIP; faults during execution surface at
+ *     the caller's next synchronisation.
+ *   - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *   - Arithmetic is binary32 with every operation rounded to nearest-even,
+ *     no fused multiply-add, subnormals kept, correctly rounded division
+ *     and square root.  Results do not depend on the launch configuration.
+ *   - Any pointer alignment is accepted; 16-byte aligned buffers take the
+ *     128-bit vector path, others a scalar path with the same results.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ZERO_OK = 0,
+  ZERO_EINVAL = -1,   /* null pointer, negative size, bad enum or flag, non-finite hyper-parameter */
+  ZERO_ERANGE = -3,   /* rank, bucket or tensor index out of range; size limit exceeded */
+  ZERO_EHIP = -4,     /* a HIP call or kernel launch failed */
+  ZERO_EOVERLAP = -5  /* an output buffer overlaps an input or another output */
+} zero_status;
+
+/* Largest number of data-parallel ranks a call accepts. */
+#define ZERO_MAX_ND 256
+
+/* ------------------------------------------------------------------ layout
+ * Bucketed flat layout ("Naive Data Parallelism": buckets; "FSDP1": flatten,
+ * concatenate, split evenly; ZeRO figure: GPU i keeps the i-th part).
+ *
+ * The n_tensors tensors form one flat stream in list order (Psi elements).
+ * The stream is cut into buckets of bucket_cap elements (the last one may be
+ * shorter; bucket_cap <= 0 puts everything in one bucket), so a tensor may
+ * straddle buckets.  Each bucket is zero-padded at its end to a multiple of
+ * n_d: padded length P_b, slice length S_b = P_b / n_d.  The padded buckets,
+ * concatenated, form the flat buffer of P = sum P_b elements that one rank's
+ * gradient bucket / the All-Gather output occupies.  Rank r owns
+ * [r*S_b, (r+1)*S_b) of every padded bucket; its shard is these slices in
+ * bucket order, S = sum S_b elements, and all per-element state (master, m,
+ * v) is stored in shard order.
+ *
+ * A layout is an immutable host object, a pure function of its arguments.
+ */
+typedef struct zero_layout zero_layout;
+
+/* numel: host array of n_tensors element counts (>= 0; zero-sized tensors are
+ * allowed).  n_d in [1, ZERO_MAX_ND], rank in [0, n_d).  On success *out
+ * receives a new layout (free it with zero_layout_destroy).
+ * Errors: ZERO_EINVAL (null, n_tensors < 0, numel < 0, n_d out of range),
+ * ZERO_ERANGE (rank out of range or Psi overflows int64). */
+int zero_layout_create(const int64_t* numel, int32_t n_tensors, int64_t bucket_cap, int32_t n_d,
+                       int32_t rank, zero_layout** out);
+void zero_layout_destroy(zero_layout* layout);
+
+/* Sizes: Psi (sum of numel), P (padded flat length), S (shard length),
+ * number of buckets, n_d, rank.  Return -1 for a null layout. */
+int64_t zero_layout_psi(const zero_layout* layout);
+int64_t zero_layout_padded(const zero_layout* layout);
+int64_t zero_layout_shard(const zero_layout* layout);
+int64_t zero_layout_n_buckets(const zero_layout* layout);
+int32_t zero_layout_n_d(const zero_layout* layout);
+int32_t zero_layout_rank(const zero_layout* layout);
+
+/* Bucket b: stream offset and real length, offset and padded length in the
+ * flat buffer, offset of its slice in the shard.  Null outputs are skipped.
+ * Errors: ZERO_EINVAL (null layout), ZERO_ERANGE (b out of range). */
+int zero_layout_bucket(const zero_layout* layout, int64_t b, int64_t* stream_off, int64_t* len,
+                       int64_t* padded_off, int64_t* padded_len, int64_t* shard_off);
+
+/* Tensor t: its stream offset, and the smallest shard range [lo, hi) holding
+ * every element of t that this rank owns (lo == hi: the rank holds none of
+ * it, the empty view of FSDP1's use_orig_params).  Inside the range there
+ * are no elements of other tensors; bucket padding may occur when t runs past
+ * the end of a padded bucket.  Errors as for zero_layout_bucket. */
+int zero_layout_tensor(const zero_layout* layout, int32_t t, int64_t* stream_off,
+                       int64_t* shard_lo, int64_t* shard_hi);
+
+/* ------------------------------------------------------------- bucket pack
+ * ("Naive Data Parallelism": a bucket carries the gradients of several
+ * parameters; "FSDP1": flatten + concatenate.)
+ *
+ * For every bucket b in [bucket_begin, bucket_end): copy the bf16 gradient
+ * elements of the stream range of b out of the per-tensor buffers into
+ * flat_out_dev[padded_off_b ...] and write +0 into the bucket's padding.
+ * Elements of flat_out_dev outside these buckets are not touched.
+ *
+ * tensor_grads_dev: HOST array of n_tensors DEVICE pointers, tensor t holding
+ * numel[t] contiguous bf16 values; entries of tensors with no element in the
+ * bucket range may be NULL.  flat_out_dev: P elements.  Sources must not
+ * overlap flat_out_dev.
+ * Errors: ZERO_EINVAL, ZERO_ERANGE (bucket range), ZERO_EOVERLAP, ZERO_EHIP. */
+int zero_bucket_pack(const zero_layout* layout, const uint16_t* const* tensor_grads_dev,
+                     int64_t bucket_begin, int64_t bucket_end, uint16_t* flat_out_dev,
+                     hipStream_t stream);
+
+/* ----------------------------------------------------- no_sync accumulation
+ * ("Naive Data Parallelism": accumulate micro-batch gradients locally; with
+ * n equal micro-batches of sample-mean losses divide each by n.)
+ *
+ * For i in [0, n):  a = (flags & ZERO_ACC_OVERWRITE) ? scale*g[i]
+ *                                                    : acc[i] + scale*g[i]
+ * (product and sum each rounded once); then, unless ZERO_ACC_NO_STORE,
+ * acc[i] = a; if ZERO_ACC_EMIT_BF16, bf16_out[i] = bf16(a) (round to nearest
+ * even).  scale is typically 1/n_micro.
+ *
+ * acc_dev: n floats (may be NULL only with OVERWRITE|NO_STORE);
+ * grad_dev: n bf16; bf16_out_dev: n bf16, required iff EMIT_BF16, and must
+ * not overlap grad_dev or acc_dev.  grad_dev must not overlap acc_dev.
+ * NO_STORE requires EMIT_BF16.  Errors: ZERO_EINVAL, ZERO_EOVERLAP, ZERO_EHIP. */
+#define ZERO_ACC_OVERWRITE 1u
+#define ZERO_ACC_EMIT_BF16 2u
+#define ZERO_ACC_NO_STORE 4u
+int zero_grad_accumulate(float* acc_dev, const uint16_t* grad_dev, int64_t n, float scale,
+                         uint32_t flags, uint16_t* bf16_out_dev, hipStream_t stream);
+
+/* ---------------------------------------------------------- shard step
+ * ("Zero Redundancy Optimizer (ZeRO)": Reduce-Scatter with averaging, the
+ * element-wise AdamW update of the owned slice, All-Gather of the updated
+ * parameters, or for ZeRO-3 keeping the updated shard in place.)
+ *
+ * For every shard index i of this rank, in binary32:
+ *   a  = bf16->f32(G_0[i]);  a = a + bf16->f32(G_q[i])  for q = 1..n_d-1
+ *   g  = a / n_d
+ *   m' = B1*m + C1*g ;  v' = B2*v + C2*(g*g)
+ *   d  = sqrt(v')*rho + E ;  th' = a_wd*th - s*(m'/d) ;  p = bf16(th')
+ * with per-call scalars computed in binary64 and rounded once to binary32:
+ *   s = lr/(1-beta1^t), rho = 1/sqrt(1-beta2^t), a_wd = 1 - lr*weight_decay,
+ *   B1 = beta1, C1 = 1-beta1, B2 = beta2, C2 = 1-beta2, E = eps
+ * (AdamW with decoupled weight decay, bias correction, eps outside the root.)
+ *
+ * t: 1-based index of this step (>= 1).
+ * rank_grads_dev: HOST array of n_d DEVICE pointers to bf16 contributions:
+ *   ZERO_GRAD_COMPACT: each holds S values in shard order (the rank's slice
+ *                      as a Reduce-Scatter would deliver it);
+ *   ZERO_GRAD_FLAT:    each is a whole padded flat buffer of P values (a
+ *                      rank's gradient bucket buffer); slice r is read.
+ * master_dev, exp_avg_dev, exp_avg_sq_dev: S floats each, updated in place.
+ * param_out_dev: ZERO_OUT_AG_SLOT: the P-element All-Gather buffer; only
+ *                      this rank's slice of each bucket is written;
+ *                ZERO_OUT_SHARD:   the S-element bf16 shard, overwritten in
+ *                      place (ZeRO-3).
+ * reduced_grad_out_dev: NULL, or S floats receiving g (for verification).
+ * Outputs must not overlap each other or any input (ZERO_EOVERLAP).
+ * Errors: ZERO_EINVAL (null pointer, bad enum, t < 1, hyper-parameters not
+ * finite or betas outside [0, 1)), ZERO_EOVERLAP, ZERO_EHIP. */
+typedef struct {
+  double lr, beta1, beta2, eps, weight_decay;
+} zero_adamw;
+
+#define ZERO_GRAD_COMPACT 0
+#define ZERO_GRAD_FLAT 1
+#define ZERO_OUT_AG_SLOT 0
+#define ZERO_OUT_SHARD 1
+
+int zero_shard_step(const zero_layout* layout, const zero_adamw* hp, int64_t t,
+                    const uint16_t* const* rank_grads_dev, int32_t grad_layout, float* master_dev,
+                    float* exp_avg_dev, float* exp_avg_sq_dev, uint16_t* param_out_dev,
+                    int32_t out_mode, float* reduced_grad_out_dev, hipStream_t stream);
+
+/* Same as zero_shard_step with an explicit launch shape, for tuning and for
+ * checking that results do not depend on it.  blocks <= 0 and threads <= 0
+ * pick the defaults; threads must be a multiple of 64 and at most 1024;
+ * path: 0 = automatic, 1 = force the scalar kernel.  Errors as above, plus
+ * ZERO_EINVAL for a bad launch shape. */
+typedef struct {
+  int32_t blocks;
+  int32_t threads;
+  int32_t path;
+} zero_launch;
+
+int zero_shard_step_ex(const zero_layout* layout, const zero_adamw* hp, int64_t t,
+                       const uint16_t* const* rank_grads_dev, int32_t grad_layout,
+                       float* master_dev, float* exp_avg_dev, float* exp_avg_sq_dev,
+                       uint16_t* param_out_dev, int32_t out_mode, float* reduced_grad_out_dev,
+                       const zero_launch* launch, hipStream_t stream);
+
+/* Per-call binary32 scalars for step t, in the order
+ * {s, rho, a_wd, B1, C1, B2, C2, E}.  Errors: ZERO_EINVAL. */
+int zero_step_scalars(const zero_adamw* hp, int64_t t, float out[8]);
+
+/* Static description of a status code. */
+const char* zero_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_SHARD_H */

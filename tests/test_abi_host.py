@@ -1,0 +1,183 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, its layout planner agrees with the oracle's, its per-step scalars
+equal the oracle's bit for bit, and bad arguments are rejected before any
+GPU work.  No kernel is launched here."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import fsdp_sharded_optimizer_step_amd as z
+import oracle
+from fsdp_sharded_optimizer_step_amd import binding
+from synth import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "zero_shard.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zero_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = z.load()
+    names = header_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_package_has_no_oracle_or_fallback_imports():
+    pkg = os.path.join(ROOT, "fsdp_sharded_optimizer_step_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "oracle" not in src, fn
+            assert "import synth" not in src, fn
+
+
+def _layout_matches(numel, cap, n_d):
+    pl = oracle.plan(numel, cap, n_d)
+    for r in range(n_d):
+        L = z.Layout(numel, cap, n_d, r)
+        assert (L.psi, L.padded, L.shard, L.n_buckets) == (sum(numel), pl.padded_total,
+                                                           pl.shard_len, pl.n_buckets)
+        got = np.array(L.buckets(), dtype=np.int64).reshape(-1, 5)
+        exp = np.stack([pl.stream_off, pl.len, pl.padded_off, pl.padded_len, pl.shard_off], 1)
+        assert np.array_equal(got, exp)
+        lo, hi = pl.tensor_ranges(r)
+        for t in range(len(numel)):
+            so, a, b = L.tensor(t)
+            assert so == sum(numel[:t])
+            assert (a, b) == (lo[t], hi[t]) or (a == b and lo[t] == hi[t])
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_layout_agrees_with_oracle_random(seed):
+    rng = np.random.default_rng(1000 + seed)
+    numel = [int(v) for v in rng.integers(0, 60, int(rng.integers(1, 9)))]
+    cap = int(rng.choice([0, 1, 5, 16, 33, 64, 1000]))
+    n_d = int(rng.choice([1, 2, 3, 4, 7, 8, 64]))
+    _layout_matches(numel, cap, n_d)
+
+
+@pytest.mark.parametrize("name", ["flat1m", "gpt2s", "accum1p3b"])
+def test_layout_agrees_with_oracle_workloads(name):
+    w = workloads.get(name)
+    _layout_matches(w.numel, w.cap, w.n_d)
+
+
+@pytest.mark.parametrize("name", ["llama8b", "llama70b", "llama70b_t"])
+def test_layout_agrees_with_oracle_large(name):
+    w = workloads.get(name)
+    pl = oracle.plan(w.numel, w.cap, w.n_d)
+    L = z.Layout(w.numel, w.cap, w.n_d, w.rank)
+    assert (L.padded, L.shard, L.n_buckets) == (pl.padded_total, pl.shard_len, pl.n_buckets)
+    for b in (0, 1, pl.n_buckets // 2, pl.n_buckets - 1):
+        assert L.bucket(b) == (pl.stream_off[b], pl.len[b], pl.padded_off[b], pl.padded_len[b],
+                               pl.shard_off[b])
+    lo, hi = pl.tensor_ranges(w.rank)
+    for t in range(len(w.numel)):
+        _, a, b = L.tensor(t)
+        assert (a, b) == (lo[t], hi[t]) or (a == b and lo[t] == hi[t])
+
+
+@pytest.mark.parametrize("t", [1, 2, 10, 101, 1001, 10 ** 6])
+@pytest.mark.parametrize("hp", [dict(), dict(lr=3e-4, beta1=0.8, beta2=0.999, eps=1e-6,
+                                             weight_decay=0.0), dict(beta1=0.0, beta2=0.0)])
+def test_step_scalars_equal_oracle(t, hp):
+    got = np.array(z.zero_step_scalars(z.AdamW(**hp), t), np.float32)
+    exp = oracle.step_scalars(oracle.AdamW(**hp), t)
+    assert np.array_equal(got.view(np.uint32), exp.view(np.uint32))
+
+
+def test_layout_errors():
+    lib = z.load()
+    h = C.c_void_p()
+    arr = (C.c_int64 * 2)(5, 7)
+    assert lib.zero_layout_create(arr, 2, 4, 0, 0, C.byref(h)) == z.binding.ZERO_EINVAL
+    assert lib.zero_layout_create(arr, 2, 4, 257, 0, C.byref(h)) == z.binding.ZERO_EINVAL
+    assert lib.zero_layout_create(arr, 2, 4, 4, 4, C.byref(h)) == z.binding.ZERO_ERANGE
+    assert lib.zero_layout_create(arr, 2, 4, 4, -1, C.byref(h)) == z.binding.ZERO_ERANGE
+    assert lib.zero_layout_create(None, 2, 4, 4, 0, C.byref(h)) == z.binding.ZERO_EINVAL
+    neg = (C.c_int64 * 2)(5, -1)
+    assert lib.zero_layout_create(neg, 2, 4, 4, 0, C.byref(h)) == z.binding.ZERO_EINVAL
+    big = (C.c_int64 * 2)(2 ** 61, 2 ** 61)
+    assert lib.zero_layout_create(big, 2, 4, 4, 0, C.byref(h)) == z.binding.ZERO_ERANGE
+    L = z.Layout([5, 7], 4, 4, 1)
+    with pytest.raises(z.ZeroError):
+        L.bucket(L.n_buckets)
+    with pytest.raises(z.ZeroError):
+        L.tensor(2)
+    e = z.Layout([], 4, 4, 1)
+    assert (e.psi, e.padded, e.shard, e.n_buckets) == (0, 0, 0, 0)
+
+
+def test_step_argument_errors_before_launch():
+    """Invalid calls fail validation on the host; nothing reaches the GPU."""
+    lib = z.load()
+    L = z.Layout([64], 0, 2, 0)
+    hp = binding._AdamW(1e-3, 0.9, 0.95, 1e-8, 0.1)
+    fake = [C.c_void_p(0x1000 * (k + 1)) for k in range(8)]
+    g = (C.c_void_p * 2)(0x100000, 0x200000)
+
+    def step(layout=L.handle, hp_=hp, t=1, grads=g, gl=0, master=0x300000, m=0x400000,
+             v=0x500000, p=0x600000, om=1, gout=None):
+        return lib.zero_shard_step(layout, C.byref(hp_) if hp_ is not None else None, t, grads,
+                                   gl, master, m, v, p, om, gout, None)
+
+    E = z.binding
+    assert step(layout=None) == E.ZERO_EINVAL
+    assert step(hp_=None) == E.ZERO_EINVAL
+    assert step(t=0) == E.ZERO_EINVAL
+    assert step(gl=2) == E.ZERO_EINVAL
+    assert step(om=5) == E.ZERO_EINVAL
+    assert step(master=None) == E.ZERO_EINVAL
+    assert step(grads=(C.c_void_p * 2)(0x100000, None)) == E.ZERO_EINVAL
+    assert step(hp_=binding._AdamW(float("nan"), 0.9, 0.95, 1e-8, 0.1)) == E.ZERO_EINVAL
+    assert step(hp_=binding._AdamW(1e-3, 1.0, 0.95, 1e-8, 0.1)) == E.ZERO_EINVAL
+    assert step(hp_=binding._AdamW(1e-3, 0.9, -0.1, 1e-8, 0.1)) == E.ZERO_EINVAL
+    assert step(hp_=binding._AdamW(1e-3, 0.9, 0.95, float("inf"), 0.1)) == E.ZERO_EINVAL
+    # overlapping outputs / inputs
+    assert step(m=0x300000 + 16) == E.ZERO_EOVERLAP
+    assert step(p=0x500000 + 2) == E.ZERO_EOVERLAP
+    assert step(grads=(C.c_void_p * 2)(0x100000, 0x400000 + 4)) == E.ZERO_EOVERLAP
+    assert step(gout=0x600000 + 8) == E.ZERO_EOVERLAP
+    # bad launch shapes
+    bad = binding._Launch(0, 100, 0)
+    rc = lib.zero_shard_step_ex(L.handle, C.byref(hp), 1, g, 0, 0x300000, 0x400000, 0x500000,
+                                0x600000, 1, None, C.byref(bad), None)
+    assert rc == E.ZERO_EINVAL
+    # empty shard: nothing to do, succeeds without touching the GPU
+    L0 = z.Layout([], 0, 2, 0)
+    assert step(layout=L0.handle) == E.ZERO_OK
+    del fake
+
+
+def test_accumulate_and_pack_argument_errors():
+    lib = z.load()
+    E = z.binding
+    assert lib.zero_grad_accumulate(0x1000, 0x2000, -1, 1.0, 0, None, None) == E.ZERO_EINVAL
+    assert lib.zero_grad_accumulate(0x1000, 0x2000, 8, 1.0, 8, None, None) == E.ZERO_EINVAL
+    assert lib.zero_grad_accumulate(0x1000, 0x2000, 8, 1.0, E.ACC_NO_STORE, None, None) == E.ZERO_EINVAL
+    assert lib.zero_grad_accumulate(0x1000, 0x2000, 8, 1.0, E.ACC_EMIT_BF16, None, None) == E.ZERO_EINVAL
+    assert lib.zero_grad_accumulate(None, 0x2000, 8, 1.0, 0, None, None) == E.ZERO_EINVAL
+    assert lib.zero_grad_accumulate(0x1000, 0x1000 + 4, 8, 1.0, 0, None, None) == E.ZERO_EOVERLAP
+    assert lib.zero_grad_accumulate(0x1000, 0x2000, 8, 1.0, E.ACC_EMIT_BF16, 0x2000 + 2,
+                                    None) == E.ZERO_EOVERLAP
+    assert lib.zero_grad_accumulate(0x1000, 0x2000, 0, 1.0, 0, None, None) == E.ZERO_OK
+    L = z.Layout([10, 20], 8, 2, 0)
+    arr = (C.c_void_p * 2)(0x10000, None)
+    assert lib.zero_bucket_pack(L.handle, arr, 0, 5, 0x20000, None) == E.ZERO_ERANGE
+    assert lib.zero_bucket_pack(L.handle, arr, 2, 1, 0x20000, None) == E.ZERO_ERANGE
+    assert lib.zero_bucket_pack(L.handle, arr, 0, 2, None, None) == E.ZERO_EINVAL
+    # tensor 1 has elements in bucket 1 but its pointer is NULL
+    assert lib.zero_bucket_pack(L.handle, arr, 0, 2, 0x20000, None) == E.ZERO_EINVAL
+    ov = (C.c_void_p * 2)(0x10000, 0x20000 + 6)
+    assert lib.zero_bucket_pack(L.handle, ov, 0, 4, 0x20000, None) == E.ZERO_EOVERLAP
+    assert lib.zero_bucket_pack(L.handle, arr, 1, 1, 0x20000, None) == E.ZERO_OK

@@ -1,0 +1,446 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.
+
+Bars (the update's stated tolerances): reduced gradients bit-exact; fp32
+master / m / v within 1e-6 relative; bf16 parameters within 1 ulp.  The
+kernels follow the oracle's operation order, so the tests also report how
+many values match exactly, and the bit-exactness of every output is asserted
+where the design claims it (small full-compare cases).
+"""
+import numpy as np
+import pytest
+import torch
+
+import fsdp_sharded_optimizer_step_amd as z
+import oracle
+import synth
+from synth import workloads
+
+from gpu_cases import (CANARY, DEV, Case, assert_bf16_close, assert_bitwise, assert_f32_close,
+                       sample_indices, u16)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _free_gpu_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_smoke_entry():
+    import __graft_entry__
+    __graft_entry__.smoke()
+
+
+# ------------------------------------------------------------------ workloads
+def run_steps(case: Case, full_check_steps=()):
+    w = case.w
+    case.init_state_gpu()
+    case.init_state_oracle()
+    for k in range(w.n_steps):
+        t = w.t_first + k
+        say(f"  {w.name}: step t={t}")
+        grads = case.grads_gpu(t)
+        case.step_gpu(t, grads)
+        del grads
+        case.step_oracle(t, case.grads_oracle(t))
+        torch.cuda.synchronize()
+        if k + 1 == w.n_steps or t in full_check_steps:
+            stats = case.compare(f"{w.name} t={t}")
+            say(f"  {w.name} t={t}: exact matches {stats} of {case.o_g.size}")
+    case.check_canaries()
+    return stats
+
+
+def test_flat1m_ten_steps_bit_exact():
+    """Flat 1,048,576-parameter shard, N_d = 4, rank 3, 10 steps; every shard
+    element compared after every step, bit for bit."""
+    case = Case(workloads.get("flat1m"))
+    case.init_state_gpu()
+    case.init_state_oracle()
+    w = case.w
+    for t in range(1, 11):
+        case.step_gpu(t, case.grads_gpu(t))
+        case.step_oracle(t, case.grads_oracle(t))
+        torch.cuda.synchronize()
+        case.compare(f"t={t}")
+        assert_bitwise(case.master.cpu().numpy(), case.o_master, "master")
+        assert_bitwise(case.m.cpu().numpy(), case.o_m, "exp_avg")
+        assert_bitwise(case.v.cpu().numpy(), case.o_v, "exp_avg_sq")
+        assert_bitwise(u16(case.pout)[case.flat_pos], case.o_p, "param")
+    case.check_canaries(n_probe=1 << 22)
+    assert w.n_steps == 10
+
+
+def test_gpt2s_pack_matches_oracle():
+    """GPT-2-small list, 25 MiB buckets, N_d = 8: one rank's packed padded
+    flat buffer equals the oracle's pack of the same per-tensor grads."""
+    w = workloads.get("gpt2s")
+    case = Case(w, sample_idx=np.arange(8))
+    tsegs = synth.tensor_segments(w.numel)
+    key = synth.key(w.name, "grad", 2, 0, 1)
+    tens = [torch.empty(n, dtype=torch.int16, device=DEV) for n in w.numel]
+    for t, n in enumerate(w.numel):
+        synth.fill_device(tens[t], tsegs[t], key, *w.grad)
+    flat = torch.full((case.P,), CANARY, dtype=torch.int16, device=DEV)
+    z.zero_bucket_pack(case.L, tens, flat)
+    torch.cuda.synchronize()
+    host_t = [u16(t) for t in tens]
+    exp = oracle.pack(host_t, case.pl)
+    assert_bitwise(u16(flat), exp, "packed flat buffer")
+
+
+def test_gpt2s_ten_steps_full():
+    case = Case(workloads.get("gpt2s"))
+    run_steps(case, full_check_steps=(1,))
+
+
+@pytest.mark.timeout(600)
+def test_accum1p3b_sampled():
+    """1.3e9 flat parameters, N_d = 8: each rank accumulates 4 micro-batches
+    scaled by 1/4 (no_sync), emits its bf16 contribution, then one step at
+    t = 101.  Full size on the GPU; the oracle checks a sample."""
+    w = workloads.get("accum1p3b")
+    case = Case(w)
+    case.__init__(w, sample_idx=sample_indices(case.S, case.pl))
+    case.init_state_gpu()
+    case.init_state_oracle()
+    S = case.S
+    acc = torch.empty(S, dtype=torch.float32, device=DEV)
+    contribs, o_contribs = [], []
+    for q in range(w.n_d):
+        say(f"  accumulate rank {q}")
+        g_out = torch.empty(S, dtype=torch.int16, device=DEV)
+        micro = torch.empty(S, dtype=torch.int16, device=DEV)
+        o_acc = np.zeros(case.idx.size, np.float32)
+        o_out = None
+        for k in range(w.n_micro):
+            key = synth.key(w.name, "micro_grad", q, k, w.t_first)
+            synth.fill_device(micro, case.segs, key, *w.micro_grad)
+            last = k == w.n_micro - 1
+            flags = (z.ACC_OVERWRITE if k == 0 else 0) | (z.ACC_EMIT_BF16 | z.ACC_NO_STORE if last else 0)
+            z.zero_grad_accumulate(acc, micro, 1.0 / w.n_micro, flags, g_out if last else None)
+            o_micro = synth.values_at(case.stream_pos, key, *w.micro_grad, synth.OUT_BF16)
+            o_out = oracle.accumulate(o_acc, o_micro, 1.0 / w.n_micro, overwrite=(k == 0),
+                                      store_acc=not last, emit=last)
+        contribs.append(g_out)
+        o_contribs.append(o_out)
+        torch.cuda.synchronize()
+        assert_bitwise(case.gather(g_out, case.idx).view(np.uint16), o_out, f"contribution {q}")
+    del micro, acc
+    say("  step t=101")
+    case.step_gpu(w.t_first, contribs)
+    case.step_oracle(w.t_first, o_contribs)
+    torch.cuda.synchronize()
+    stats = case.compare("accum1p3b")
+    say(f"  accum1p3b: exact matches {stats} of {case.idx.size}")
+    case.check_canaries()
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_sampled():
+    """Llama-3-8B list, 613 buckets of 25 MiB, N_d = 8, rank 7 (1.0e9-element
+    shard, 16 GB of bf16 contributions), 10 steps from m = v = 0; sampled."""
+    w = workloads.get("llama8b")
+    case = Case(w)
+    case.__init__(w, sample_idx=sample_indices(case.S, case.pl))
+    stats = run_steps(case)
+    assert stats["param"] > 0.99 * case.idx.size
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["llama70b", "llama70b_t"])
+def test_llama70b_sampled(name):
+    """Llama-70B list, N_d = 64, rank 63, ZeRO-3 in place, t = 1001: 141 GB of
+    bf16 contributions; sampled.  The 12.5M-element cut leaves 32 padded
+    elements per bucket in this rank's slice."""
+    w = workloads.get(name)
+    case = Case(w)
+    idx = sample_indices(case.S, case.pl)
+    case.__init__(w, sample_idx=idx)
+    run_steps(case)
+    if name == "llama70b_t":
+        # padding stays +0 in every output
+        pads = case.idx[case.stream_pos < 0]
+        assert pads.size > 0
+        for buf in (case.master, case.m, case.v):
+            assert not case.gather(buf, pads).view(np.uint32).any()
+        assert not case.gather(case.pout, pads).any()
+
+
+# ------------------------------------------------------------------ edge cases
+EDGE = [
+    # numel, cap, n_d, rank, grad_layout, out_mode
+    ([1000, 37, 4096, 3], 1500, 4, 3, "flat", "ag_slot"),
+    ([1000, 37, 4096, 3], 1500, 4, 0, "compact", "shard"),
+    ([17], 0, 1, 0, "flat", "ag_slot"),                     # N_d = 1: no reduction
+    ([5, 0, 123, 64], 40, 3, 2, "flat", "ag_slot"),         # non-power-of-two N_d, empty tensor
+    ([999, 1001], 0, 5, 4, "compact", "ag_slot"),
+    ([4096 * 7 + 5], 4096, 7, 6, "flat", "shard"),
+    ([70000, 3], 16384, 8, 7, "flat", "ag_slot"),           # ragged last bucket (slice % 8 != 0)
+    ([50000], 8008, 8, 3, "flat", "ag_slot"),               # slice 1001: unaligned flat slots
+    ([20000, 20001], 0, 16, 15, "compact", "ag_slot"),
+    ([65536 + 13], 0, 32, 31, "flat", "ag_slot"),
+    ([64 * 300 + 1], 6400, 64, 63, "compact", "shard"),     # N_d = 64 with padded tails
+    ([64 * 300 + 1], 6400, 64, 0, "flat", "ag_slot"),
+    ([100 * 97], 0, 100, 99, "compact", "shard"),           # generic rank count
+    ([256 * 33 + 7], 0, 256, 255, "flat", "ag_slot"),       # largest rank count
+    ([8], 0, 8, 5, "flat", "ag_slot"),                      # one element per rank
+    ([3], 0, 8, 7, "flat", "ag_slot"),                      # this rank holds only padding
+]
+
+
+def _edge_case(numel, cap, n_d, rank, gl, om, t=3):
+    w = workloads.Workload("edge", numel, cap, n_d, rank, gl, om, t, 1, ("normal", 1e-3),
+                           ("normal", 0.02), ("normal", 1e-4), ("absnormal", 1e-6))
+    w.name = "flat1m"  # reuse a workload id for the generator keys
+    return Case(w)
+
+
+@pytest.mark.parametrize("numel,cap,n_d,rank,gl,om", EDGE)
+def test_edge_cases_full_compare(numel, cap, n_d, rank, gl, om):
+    case = _edge_case(numel, cap, n_d, rank, gl, om)
+    say(f"  edge numel={numel} cap={cap} n_d={n_d} r={rank} {gl} {om}: S={case.S}")
+    case.init_state_gpu()
+    case.init_state_oracle()
+    for t in (1, 2, 3):
+        case.step_gpu(t, case.grads_gpu(t))
+        case.step_oracle(t, case.grads_oracle(t))
+    torch.cuda.synchronize()
+    case.compare("edge")
+    for a, b in ((case.master, case.o_master), (case.m, case.o_m), (case.v, case.o_v)):
+        assert_bitwise(a.cpu().numpy(), b, "state")
+    pos = case.flat_pos if om == "ag_slot" else np.arange(case.S)
+    assert_bitwise(u16(case.pout)[pos], case.o_p, "param")
+    case.check_canaries(n_probe=4096)
+
+
+def test_empty_shard_is_a_no_op():
+    L = z.Layout([], 0, 4, 0)
+    e = torch.empty(0, dtype=torch.float32, device=DEV)
+    h = torch.empty(0, dtype=torch.int16, device=DEV)
+    z.zero_shard_step(L, z.AdamW(), 1, [h] * 4, z.GRAD_COMPACT, e, e.clone(), e.clone(), h.clone(),
+                      z.OUT_SHARD)
+    torch.cuda.synchronize()
+
+
+def test_all_ranks_assemble_the_unsharded_update():
+    """Every rank steps its own shard into its All-Gather slot of one shared
+    buffer; the assembled buffer and states equal the oracle's update of the
+    whole padded flat buffer (sharded == unsharded)."""
+    numel, cap, n_d, t = [301, 77, 1024, 5, 900], 640, 4, 2
+    pl = oracle.plan(numel, cap, n_d)
+    P = pl.padded_total
+    rng = np.random.default_rng(9)
+    flats_h = []
+    for q in range(n_d):
+        ts = [synth.fill_host(n, synth.OUT_BF16, [(0, sum(numel[:k]), n, 0)],
+                              synth.key("gpt2s", "grad", q, 0, t), "normal", 1e-3)
+              for k, n in enumerate(numel)]
+        flats_h.append(oracle.pack(ts, pl))
+    th = (rng.standard_normal(P) * 0.02).astype(np.float32)
+    m0 = (rng.standard_normal(P) * 1e-4).astype(np.float32)
+    v0 = np.abs(rng.standard_normal(P) * 1e-6).astype(np.float32)
+    pads = np.ones(P, bool)
+    for r in range(n_d):
+        f, s = pl.map(r, np.arange(pl.shard_len))
+        pads[f[s >= 0]] = False
+    th[pads] = 0
+    m0[pads] = 0
+    v0[pads] = 0
+    full = [th.copy(), m0.copy(), v0.copy()]
+    p_full, _ = oracle.shard_step(flats_h, *full, oracle.AdamW(), t)
+    flats = [torch.from_numpy(f.view(np.int16)).to(DEV) for f in flats_h]
+    ag = torch.full((P,), CANARY, dtype=torch.int16, device=DEV)
+    got = [np.zeros(P, np.float32) for _ in range(3)]
+    for r in range(n_d):
+        L = z.Layout(numel, cap, n_d, r)
+        f, _ = pl.map(r, np.arange(pl.shard_len))
+        st = [torch.from_numpy(a[f].copy()).to(DEV) for a in (th, m0, v0)]
+        z.zero_shard_step(L, z.AdamW(), t, flats, z.GRAD_FLAT, *st, ag, z.OUT_AG_SLOT)
+        torch.cuda.synchronize()
+        for dst, src in zip(got, st):
+            dst[f] = src.cpu().numpy()
+    assert_bitwise(u16(ag), p_full, "assembled All-Gather buffer")
+    for a, b in zip(got, full):
+        assert_bitwise(a, b, "assembled state")
+
+
+@pytest.mark.parametrize("launch", [(1, 64, 0), (7, 192, 0), (64, 256, 0), (3000, 128, 0),
+                                    (0, 0, 1), (5, 64, 1), (100000, 256, 0)])
+def test_launch_shape_invariance(launch):
+    """Results are bit-identical for any grid / block size and for the scalar
+    path (no reduction across lanes, fixed rank order)."""
+    numel, cap, n_d, rank = [300_000, 12_345, 777], 65_536, 8, 6
+    outs = []
+    for lc in (None, launch):
+        case = _edge_case(numel, cap, n_d, rank, "flat", "ag_slot")
+        case.init_state_gpu()
+        grads = case.grads_gpu(5)
+        case.step_gpu(5, grads, launch=lc)
+        torch.cuda.synchronize()
+        outs.append([case.master.cpu().numpy(), case.m.cpu().numpy(), case.v.cpu().numpy(),
+                     u16(case.pout), case.gout.cpu().numpy()])
+    for a, b in zip(*outs):
+        assert_bitwise(a, b, f"launch {launch}")
+
+
+def test_misaligned_buffers_take_the_scalar_path():
+    """Buffers offset by one element (2 or 4 bytes from 16-byte alignment)
+    give the same results as the oracle."""
+    numel, n_d, t = [5000], 4, 2
+    pl = oracle.plan(numel, 0, n_d)
+    S = pl.shard_len
+    rng = np.random.default_rng(11)
+    gh = [(rng.standard_normal(S) * 1e-3).astype(np.float32) for _ in range(n_d)]
+    gh = [oracle.round_bf16(g) for g in gh]
+    th = (rng.standard_normal(S) * 0.02).astype(np.float32)
+    m0 = (rng.standard_normal(S) * 1e-4).astype(np.float32)
+    v0 = np.abs(rng.standard_normal(S) * 1e-6).astype(np.float32)
+
+    def off(a, dt):
+        buf = torch.empty(a.size + 1, dtype=dt, device=DEV)
+        view = buf[1:]
+        view.copy_(torch.from_numpy(a.view(np.int16) if dt == torch.int16 else a))
+        return view
+
+    L = z.Layout(numel, 0, n_d, 1)
+    grads = [off(g, torch.int16) for g in gh]
+    st = [off(a.copy(), torch.float32) for a in (th, m0, v0)]
+    p = torch.empty(S + 1, dtype=torch.int16, device=DEV)[1:]
+    z.zero_shard_step(L, z.AdamW(), t, grads, z.GRAD_COMPACT, *st, p, z.OUT_SHARD)
+    torch.cuda.synchronize()
+    o = [th.copy(), m0.copy(), v0.copy()]
+    ep, _ = oracle.shard_step(gh, *o, oracle.AdamW(), t)
+    for a, b in zip(st, o):
+        assert_bitwise(a.cpu().numpy(), b, "state")
+    assert_bitwise(u16(p), ep, "param")
+
+
+def test_nonfinite_gradients_propagate_elementwise():
+    n_d, S, t = 4, 4096, 1
+    rng = np.random.default_rng(12)
+    gh = [oracle.round_bf16((rng.standard_normal(S) * 1e-3).astype(np.float32))
+          for _ in range(n_d)]
+    gh[2][100] = 0x7F80   # +inf
+    gh[1][200] = 0xFFC1   # NaN
+    gh[0][300] = 0x7F80
+    gh[3][300] = 0xFF80   # inf - inf = NaN
+    th = (rng.standard_normal(S) * 0.02).astype(np.float32)
+    L = z.Layout([S * n_d], 0, n_d, 0)
+    grads = [torch.from_numpy(g.view(np.int16)).to(DEV) for g in gh]
+    st = [torch.from_numpy(a).to(DEV) for a in (th.copy(), np.zeros(S, np.float32),
+                                                 np.zeros(S, np.float32))]
+    p = torch.empty(S, dtype=torch.int16, device=DEV)
+    gout = torch.empty(S, dtype=torch.float32, device=DEV)
+    z.zero_shard_step(L, z.AdamW(), t, grads, z.GRAD_COMPACT, *st, p, z.OUT_SHARD, gout)
+    torch.cuda.synchronize()
+    o = [th.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32)]
+    ep, eg = oracle.shard_step(gh, *o, oracle.AdamW(), t, want_grad=True)
+    gm = st[0].cpu().numpy()
+    bad = np.isnan(gm) | np.isinf(gm)
+    assert set(np.flatnonzero(bad)) <= {100, 200, 300}
+    ok = np.ones(S, bool)
+    ok[[100, 200, 300]] = False
+    assert_bitwise(gm[ok], o[0][ok], "finite elements")
+    assert np.isnan(gout.cpu().numpy()[[200, 300]]).all()
+    assert np.isinf(gout.cpu().numpy()[100])
+    assert_bitwise(u16(p)[ok], ep[ok], "finite params")
+
+
+def test_repeat_calls_are_deterministic():
+    outs = []
+    for _ in range(2):
+        case = _edge_case([123_457, 99], 50_000, 8, 3, "compact", "ag_slot")
+        case.init_state_gpu()
+        case.step_gpu(4, case.grads_gpu(4))
+        torch.cuda.synchronize()
+        outs.append([case.master.cpu().numpy(), u16(case.pout), case.gout.cpu().numpy()])
+    for a, b in zip(*outs):
+        assert_bitwise(a, b, "repeat")
+
+
+# ------------------------------------------------------------------ accumulate
+@pytest.mark.parametrize("n,offset", [(1 << 20, 0), ((1 << 20) + 5, 0), (1003, 1), (7, 0)])
+def test_accumulate_modes_match_oracle(n, offset):
+    rng = np.random.default_rng(13)
+    g = [oracle.round_bf16((rng.standard_normal(n) * 2e-3).astype(np.float32)) for _ in range(4)]
+    acc0 = rng.standard_normal(n).astype(np.float32)
+
+    def dev(a, dt):
+        buf = torch.empty(a.size + offset, dtype=dt, device=DEV)[offset:]
+        buf.copy_(torch.from_numpy(a.view(np.int16) if dt == torch.int16 else a))
+        return buf
+
+    for flags in (z.ACC_OVERWRITE, 0, z.ACC_EMIT_BF16, z.ACC_EMIT_BF16 | z.ACC_NO_STORE,
+                  z.ACC_OVERWRITE | z.ACC_EMIT_BF16,
+                  z.ACC_OVERWRITE | z.ACC_EMIT_BF16 | z.ACC_NO_STORE):
+        acc = dev(acc0.copy(), torch.float32)
+        out = dev(np.zeros(n, np.uint16), torch.int16)
+        gd = dev(g[1], torch.int16)
+        z.zero_grad_accumulate(acc, gd, 0.25, flags, out if flags & z.ACC_EMIT_BF16 else None)
+        torch.cuda.synchronize()
+        o_acc = acc0.copy()
+        emit = bool(flags & z.ACC_EMIT_BF16)
+        o_out = oracle.accumulate(o_acc, g[1], 0.25, overwrite=bool(flags & z.ACC_OVERWRITE),
+                                  store_acc=not (flags & z.ACC_NO_STORE), emit=emit)
+        assert_bitwise(acc.cpu().numpy(), o_acc, f"acc flags={flags}")
+        if emit:
+            assert_bitwise(u16(out), o_out, f"bf16 flags={flags}")
+
+
+def test_accumulate_four_micro_batches_equal_full_batch_mean_on_gpu():
+    n = (1 << 18) + 3
+    rng = np.random.default_rng(14)
+    g = [oracle.round_bf16((rng.standard_normal(n) * 2e-3).astype(np.float32)) for _ in range(4)]
+    acc = torch.full((n,), float("nan"), dtype=torch.float32, device=DEV)
+    for k in range(4):
+        z.zero_grad_accumulate(acc, torch.from_numpy(g[k].view(np.int16)).to(DEV), 0.25,
+                               z.ACC_OVERWRITE if k == 0 else 0)
+    torch.cuda.synchronize()
+    w = [oracle.widen_bf16(x) for x in g]
+    mean = (((w[0] + w[1]) + w[2]) + w[3]) / np.float32(4)
+    assert_bitwise(acc.cpu().numpy(), mean, "accumulated mean")
+
+
+# ------------------------------------------------------------------ cast
+@pytest.mark.timeout(600)
+def test_gpu_bf16_cast_exhaustive():
+    """With lr = wd = 0, zero gradients and moments, the step leaves every
+    master value unchanged and writes bf16(master): all 2^32 binary32
+    patterns, compared with the oracle's rounding."""
+    from concurrent.futures import ThreadPoolExecutor
+    hp = z.AdamW(lr=0.0, weight_decay=0.0, eps=1.0)
+    chunk = 1 << 28
+    L = z.Layout([chunk], 0, 1, 0)
+    g = torch.zeros(chunk, dtype=torch.int16, device=DEV)
+    m = torch.zeros(chunk, dtype=torch.float32, device=DEV)
+    v = torch.zeros_like(m)
+    p = torch.empty(chunk, dtype=torch.int16, device=DEV)
+    base = torch.arange(chunk, dtype=torch.int64, device=DEV)
+    sub = chunk // 16
+    with ThreadPoolExecutor(16) as ex:
+        for c in range((1 << 32) // chunk):
+            lo = c * chunk
+            signed_lo = lo - (1 << 32) if lo >= (1 << 31) else lo
+            th = (base + signed_lo).to(torch.int32).view(torch.float32).contiguous()
+            m.zero_()
+            v.zero_()
+            z.zero_shard_step(L, hp, 1, [g], z.GRAD_COMPACT, th, m, v, p, z.OUT_SHARD)
+            torch.cuda.synchronize()
+            exp = np.concatenate(list(ex.map(
+                lambda k: oracle.round_bf16_patterns(lo + k * sub, lo + (k + 1) * sub),
+                range(16))))
+            got = u16(p)
+            pats = np.arange(lo, lo + chunk, dtype=np.uint64).astype(np.uint32)
+            nan = ((pats & 0x7F800000) == 0x7F800000) & ((pats & 0x7FFFFF) != 0)
+            assert_bitwise(got[~nan], exp[~nan], f"cast chunk {c}")
+            gn = got[nan].astype(np.uint32)
+            assert (((gn & 0x7F80) == 0x7F80) & ((gn & 0x7F) != 0)).all()
+            say(f"  cast chunk {c} ok")
