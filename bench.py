@@ -115,17 +115,21 @@ def cpu_baseline(w, segs, S, target_s=12.0):
     t0 = time.perf_counter()
     oracle.shard_step(G, *st, hp, w.t_first, nthreads=threads)
     pilot = max(1e-6, time.perf_counter() - t0)
-    rate = n / pilot
-    n_target = int(min(S, max(n, rate * target_s), 96 << 20))
-    n, G, st = sample_inputs(n_target)
+    # the sample: 2^29 / N_d contiguous shard elements (64M at N_d = 8),
+    # stepped repeatedly (t advancing) until about target_s of CPU work has
+    # been timed
+    n = int(min(S, (1 << 29) // w.n_d))
+    reps = max(1, int(round(target_s / (pilot * n / (1 << 20)))))
+    n, G, st = sample_inputs(n)
     t0 = time.perf_counter()
-    oracle.shard_step(G, *st, hp, w.t_first, nthreads=threads)
+    for k in range(reps):
+        oracle.shard_step(G, *st, hp, w.t_first + k, nthreads=threads)
     dt = time.perf_counter() - t0
     del G, st
-    return {"value": n / dt, "unit": "elem/s", "cores": threads, "kind": "oracle",
+    return {"value": n * reps / dt, "unit": "elem/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} elements of the same shard (inputs generated untimed), "
-                      f"one step, {dt:.1f} s on {threads} host threads",
-            "gbps": n * (2 * w.n_d + 26) / dt / 1e9}
+                      f"{reps} consecutive steps, {dt:.1f} s on {threads} host threads",
+            "gbps": n * reps * (2 * w.n_d + 26) / dt / 1e9}
 
 
 def main():
@@ -137,6 +141,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--blocks", type=int, default=0)
     ap.add_argument("--threads", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (3 times): the known-size "
+                         "reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the shard step of one rank); "
@@ -144,6 +151,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 1 << 30,
+                          "copy_calibration_bytes_written": 1 << 30, "launches": 3}))
+        return
 
     import fsdp_sharded_optimizer_step_amd as z
     import synth
