@@ -12,16 +12,24 @@ namespace zs {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Streaming accesses: every byte is touched exactly once per call, so the
-// loads and stores carry the non-temporal hint and do not displace the
-// caches' contents.
-template <class T>
+// Streaming accesses: every byte is touched exactly once per call.  NT
+// selects the non-temporal cache hint.  Measured on MI355X, it helps the
+// read-dominated step at large N_d and costs bandwidth on the mixed
+// read/write streams (small N_d, accumulate, pack), so it is a per-kernel
+// choice.
+template <bool NT, class T>
 __device__ __forceinline__ T ld_stream(const T* p) {
-  return __builtin_nontemporal_load(p);
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
 }
-template <class T>
+template <bool NT, class T>
 __device__ __forceinline__ void st_stream(T* p, T v) {
-  __builtin_nontemporal_store(v, p);
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
 }
 
 // bf16 -> binary32 is exact: the bf16 pattern is the upper half.

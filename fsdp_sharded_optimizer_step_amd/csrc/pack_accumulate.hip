@@ -55,10 +55,10 @@ __global__ void __launch_bounds__(256) pack_kernel(const PackArgs A) {
   u32x4* dv = (u32x4*)(d + head);
   if (zeros) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int64_t k = tid; k < nv; k += T) st_stream(dv + k, z);
+    for (int64_t k = tid; k < nv; k += T) st_stream<false>(dv + k, z);
   } else {
     const u32x4* sv = (const u32x4*)(pc.src + head);
-    for (int64_t k = tid; k < nv; k += T) st_stream(dv + k, ld_stream(sv + k));
+    for (int64_t k = tid; k < nv; k += T) st_stream<false>(dv + k, ld_stream<false>(sv + k));
   }
 }
 
@@ -74,22 +74,22 @@ __global__ void __launch_bounds__(256) accum_vec_kernel(float* acc, const uint16
   const int64_t T = (int64_t)gridDim.x * blockDim.x;
   for (int64_t k = tid; k < nv; k += T) {
     const int64_t i = k << 3;
-    const u32x4 w = ld_stream((const u32x4*)(g + i));
+    const u32x4 w = ld_stream<false>((const u32x4*)(g + i));
     float a[8] = {scale * bf16_lo(w.x), scale * bf16_hi(w.x), scale * bf16_lo(w.y),
                   scale * bf16_hi(w.y), scale * bf16_lo(w.z), scale * bf16_hi(w.z),
                   scale * bf16_lo(w.w), scale * bf16_hi(w.w)};
     if (!overwrite) {
-      const f32x4 a0 = ld_stream((const f32x4*)(acc + i));
-      const f32x4 a1 = ld_stream((const f32x4*)(acc + i + 4));
+      const f32x4 a0 = ld_stream<false>((const f32x4*)(acc + i));
+      const f32x4 a1 = ld_stream<false>((const f32x4*)(acc + i + 4));
       a[0] = a0.x + a[0]; a[1] = a0.y + a[1]; a[2] = a0.z + a[2]; a[3] = a0.w + a[3];
       a[4] = a1.x + a[4]; a[5] = a1.y + a[5]; a[6] = a1.z + a[6]; a[7] = a1.w + a[7];
     }
     if (store) {
-      st_stream((f32x4*)(acc + i), f32x4{a[0], a[1], a[2], a[3]});
-      st_stream((f32x4*)(acc + i + 4), f32x4{a[4], a[5], a[6], a[7]});
+      st_stream<false>((f32x4*)(acc + i), f32x4{a[0], a[1], a[2], a[3]});
+      st_stream<false>((f32x4*)(acc + i + 4), f32x4{a[4], a[5], a[6], a[7]});
     }
     if (emit)
-      st_stream((u32x4*)(out + i), u32x4{bf16_pack2(a[0], a[1]), bf16_pack2(a[2], a[3]),
+      st_stream<false>((u32x4*)(out + i), u32x4{bf16_pack2(a[0], a[1]), bf16_pack2(a[2], a[3]),
                                          bf16_pack2(a[4], a[5]), bf16_pack2(a[6], a[7])});
   }
   const int64_t tail0 = nv << 3;

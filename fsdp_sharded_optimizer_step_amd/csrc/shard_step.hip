@@ -94,15 +94,15 @@ __device__ __forceinline__ void add8(float a[8], const u32x4 w) {
 }
 
 // Sum of the N_d contributions of 8 consecutive elements, ascending rank.
-template <int ND, int GROUP>
+template <int ND, int GROUP, bool NT>
 __device__ __forceinline__ void reduce8(float acc[8], const StepArgs<ND>& A, int64_t gi) {
-  widen8(acc, ld_stream((const u32x4*)(A.g[0] + gi)));
+  widen8(acc, ld_stream<NT>((const u32x4*)(A.g[0] + gi)));
 #pragma unroll
   for (int q0 = 1; q0 < ND; q0 += GROUP) {
     u32x4 w[GROUP];
 #pragma unroll
     for (int u = 0; u < GROUP; ++u)
-      if (q0 + u < ND) w[u] = ld_stream((const u32x4*)(A.g[q0 + u] + gi));
+      if (q0 + u < ND) w[u] = ld_stream<NT>((const u32x4*)(A.g[q0 + u] + gi));
 #pragma unroll
     for (int u = 0; u < GROUP; ++u)
       if (q0 + u < ND) add8(acc, w[u]);
@@ -110,10 +110,11 @@ __device__ __forceinline__ void reduce8(float acc[8], const StepArgs<ND>& A, int
 }
 
 // Runtime rank count (any N_d up to ZERO_MAX_ND).
+template <bool NT>
 __device__ __forceinline__ void reduce8_dyn(float acc[8], const StepArgs<ZERO_MAX_ND>& A,
                                             int64_t gi) {
-  widen8(acc, ld_stream((const u32x4*)(A.g[0] + gi)));
-  for (int q = 1; q < A.nd; ++q) add8(acc, ld_stream((const u32x4*)(A.g[q] + gi)));
+  widen8(acc, ld_stream<NT>((const u32x4*)(A.g[0] + gi)));
+  for (int q = 1; q < A.nd; ++q) add8(acc, ld_stream<NT>((const u32x4*)(A.g[q] + gi)));
 }
 
 __device__ __forceinline__ int64_t flat_of(const Region& r, int64_t e) {
@@ -149,7 +150,7 @@ __device__ __forceinline__ void step_one(const StepArgs<NP>& A, int64_t e, bool 
 template <int ND>
 using ArgsFor = StepArgs<(ND > 0 ? ND : ZERO_MAX_ND)>;
 
-template <int ND, bool MAP, int GROUP>
+template <int ND, bool MAP, int GROUP, bool NT>
 __global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND> A) {
   const int64_t n = A.reg.n;
   const int64_t nv0 = A.reg.n0 >> 3;
@@ -183,16 +184,16 @@ __global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND> A) {
 
     float acc[8];
     if constexpr (ND > 0)
-      reduce8<ND, GROUP>(acc, A, gi);
+      reduce8<ND, GROUP, NT>(acc, A, gi);
     else
-      reduce8_dyn(acc, A, gi);
+      reduce8_dyn<NT>(acc, A, gi);
 
-    const f32x4 th0 = ld_stream((const f32x4*)(A.master + i));
-    const f32x4 th1 = ld_stream((const f32x4*)(A.master + i + 4));
-    const f32x4 m0 = ld_stream((const f32x4*)(A.m + i));
-    const f32x4 m1 = ld_stream((const f32x4*)(A.m + i + 4));
-    const f32x4 v0 = ld_stream((const f32x4*)(A.v + i));
-    const f32x4 v1 = ld_stream((const f32x4*)(A.v + i + 4));
+    const f32x4 th0 = ld_stream<NT>((const f32x4*)(A.master + i));
+    const f32x4 th1 = ld_stream<NT>((const f32x4*)(A.master + i + 4));
+    const f32x4 m0 = ld_stream<NT>((const f32x4*)(A.m + i));
+    const f32x4 m1 = ld_stream<NT>((const f32x4*)(A.m + i + 4));
+    const f32x4 v0 = ld_stream<NT>((const f32x4*)(A.v + i));
+    const f32x4 v1 = ld_stream<NT>((const f32x4*)(A.v + i + 4));
     float th[8] = {th0.x, th0.y, th0.z, th0.w, th1.x, th1.y, th1.z, th1.w};
     float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
     float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -202,18 +203,18 @@ __global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND> A) {
       g[k] = average<((ND & (ND - 1)) == 0 ? ND : 0)>(acc[k], A);
       adamw(g[k], th[k], mm[k], vv[k], A.k);
     }
-    st_stream((f32x4*)(A.master + i), f32x4{th[0], th[1], th[2], th[3]});
-    st_stream((f32x4*)(A.master + i + 4), f32x4{th[4], th[5], th[6], th[7]});
-    st_stream((f32x4*)(A.m + i), f32x4{mm[0], mm[1], mm[2], mm[3]});
-    st_stream((f32x4*)(A.m + i + 4), f32x4{mm[4], mm[5], mm[6], mm[7]});
-    st_stream((f32x4*)(A.v + i), f32x4{vv[0], vv[1], vv[2], vv[3]});
-    st_stream((f32x4*)(A.v + i + 4), f32x4{vv[4], vv[5], vv[6], vv[7]});
-    st_stream((u32x4*)(A.pout + oi),
+    st_stream<NT>((f32x4*)(A.master + i), f32x4{th[0], th[1], th[2], th[3]});
+    st_stream<NT>((f32x4*)(A.master + i + 4), f32x4{th[4], th[5], th[6], th[7]});
+    st_stream<NT>((f32x4*)(A.m + i), f32x4{mm[0], mm[1], mm[2], mm[3]});
+    st_stream<NT>((f32x4*)(A.m + i + 4), f32x4{mm[4], mm[5], mm[6], mm[7]});
+    st_stream<NT>((f32x4*)(A.v + i), f32x4{vv[0], vv[1], vv[2], vv[3]});
+    st_stream<NT>((f32x4*)(A.v + i + 4), f32x4{vv[4], vv[5], vv[6], vv[7]});
+    st_stream<NT>((u32x4*)(A.pout + oi),
               u32x4{bf16_pack2(th[0], th[1]), bf16_pack2(th[2], th[3]), bf16_pack2(th[4], th[5]),
                     bf16_pack2(th[6], th[7])});
     if (A.gout) {
-      st_stream((f32x4*)(A.gout + i), f32x4{g[0], g[1], g[2], g[3]});
-      st_stream((f32x4*)(A.gout + i + 4), f32x4{g[4], g[5], g[6], g[7]});
+      st_stream<NT>((f32x4*)(A.gout + i), f32x4{g[0], g[1], g[2], g[3]});
+      st_stream<NT>((f32x4*)(A.gout + i + 4), f32x4{g[4], g[5], g[6], g[7]});
     }
   }
   // the elements after the last full vector, one per lane
@@ -269,14 +270,21 @@ int cu_count() {
 }
 
 constexpr int kDefaultThreads = 256;
-constexpr int kDefaultBlocksPerCU = 8;
+
+// Launch policy, from measurements on MI355X (see the design notes): the
+// read-dominated large-N_d step streams best with non-temporal accesses and
+// one 256-thread block per CU; the small-N_d step (one third writes) with
+// ordinary accesses and two blocks per CU.
+constexpr bool nt_for(int nd) { return nd >= 32; }
+int default_blocks_per_cu(int nd) { return nd >= 32 ? 1 : 2; }
 
 template <int ND, bool MAP>
 int launch_vec(const Call& c, const Region& reg, int blocks, int threads, hipStream_t s) {
   StepArgs<ND> A;
   fill_args(A, c, reg);
   constexpr int GROUP = (ND > 16) ? 16 : (ND > 1 ? ND - 1 : 1);
-  hipLaunchKernelGGL((step_vec_kernel<ND, MAP, GROUP>), dim3(blocks), dim3(threads), 0, s, A);
+  hipLaunchKernelGGL((step_vec_kernel<ND, MAP, GROUP, nt_for(ND)>), dim3(blocks), dim3(threads), 0,
+                     s, A);
   return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
 }
 
@@ -292,7 +300,11 @@ int dispatch_vec(const Call& c, const Region& reg, int blocks, int threads, hipS
     default: {
       StepArgs<ZERO_MAX_ND> A;
       fill_args(A, c, reg);
-      hipLaunchKernelGGL((step_vec_kernel<0, MAP, 1>), dim3(blocks), dim3(threads), 0, s, A);
+      if (c.nd >= 32)
+        hipLaunchKernelGGL((step_vec_kernel<0, MAP, 1, true>), dim3(blocks), dim3(threads), 0, s, A);
+      else
+        hipLaunchKernelGGL((step_vec_kernel<0, MAP, 1, false>), dim3(blocks), dim3(threads), 0, s,
+                           A);
       return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
     }
   }
@@ -399,7 +411,7 @@ int zero_shard_step_ex(const zero_layout* L, const zero_adamw* hp, int64_t t,
   bool aligned = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) &&
                  aligned16(param_out) && (!reduced_grad_out || aligned16(reduced_grad_out));
   for (int32_t q = 0; q < nd; ++q) aligned = aligned && aligned16(rank_grads[q]);
-  const int cap = blocks_cap > 0 ? blocks_cap : cu_count() * kDefaultBlocksPerCU;
+  const int cap = blocks_cap > 0 ? blocks_cap : cu_count() * default_blocks_per_cu(nd);
   const bool allow_vec = path == 0 && aligned;
 
   // Launch plan.  Without flat addressing the shard is one plain range.
