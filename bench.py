@@ -132,6 +132,68 @@ def cpu_baseline(w, segs, S, target_s=12.0):
             "gbps": n * reps * (2 * w.n_d + 26) / dt / 1e9}
 
 
+def aux_kernels(z, synth, workloads):
+    """Pack (gpt2s list, one rank's 124M-element flat buffer) and the no_sync
+    accumulate sequence (accum1p3b shard: 4 calls) timed with HIP events."""
+    import torch
+    dev = torch.device("cuda:0")
+    out = []
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    w = workloads.get("gpt2s")
+    L = z.Layout(w.numel, w.cap, w.n_d, w.rank)
+    tens = [torch.empty(n, dtype=torch.int16, device=dev) for n in w.numel]
+    for t, segs in zip(tens, synth.tensor_segments(w.numel)):
+        synth.fill_device(t, segs, synth.key(w.name, "grad", 0, 0, 1), *w.grad)
+    flat = torch.empty(L.padded, dtype=torch.int16, device=dev)
+    ms = timed(lambda: z.zero_bucket_pack(L, tens, flat))
+    nbytes = 2 * L.psi + 2 * L.padded
+    out.append({"kernel": "pack_kernel", "workload": "gpt2s: 148 tensors -> 124,439,808-element "
+                "flat buffer, 25 MiB buckets", "bytes_per_call": nbytes, "ms": ms,
+                "GBps": nbytes / (ms * 1e-3) / 1e9, "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
+    del tens, flat
+
+    w = workloads.get("accum1p3b")
+    L = z.Layout(w.numel, w.cap, w.n_d, w.rank)
+    S = L.shard
+    acc = torch.empty(S, dtype=torch.float32, device=dev)
+    micro = [torch.empty(S, dtype=torch.int16, device=dev) for _ in range(w.n_micro)]
+    so, ln, _, pln, sh = (list(x) for x in zip(*L.buckets()))
+    segs = synth.shard_segments(so, ln, pln, sh, w.n_d, w.rank)
+    for k, mg in enumerate(micro):
+        synth.fill_device(mg, segs, synth.key(w.name, "micro_grad", 0, k, w.t_first), *w.micro_grad)
+    emit = torch.empty(S, dtype=torch.int16, device=dev)
+
+    def seq():
+        for k in range(w.n_micro):
+            last = k == w.n_micro - 1
+            flags = (z.ACC_OVERWRITE if k == 0 else 0) | (
+                z.ACC_EMIT_BF16 | z.ACC_NO_STORE if last else 0)
+            z.zero_grad_accumulate(acc, micro[k], 1.0 / w.n_micro, flags, emit if last else None)
+
+    ms = timed(seq, reps=5)
+    nbytes = S * (6 + 10 + 10 + 8)
+    out.append({"kernel": "accum_vec_kernel", "workload": "accum1p3b: 162,500,000-element shard, "
+                "4 micro-batches (overwrite, add, add, add+emit bf16 without fp32 store)",
+                "bytes_per_call": nbytes, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
+                "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
+    del acc, micro, emit
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +201,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b", choices=sorted(WORKLOAD_LABEL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-aux", action="store_true", help="skip the pack/accumulate timings")
     ap.add_argument("--blocks", type=int, default=0)
     ap.add_argument("--threads", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -210,10 +273,20 @@ def main():
     print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, kernel avg {k_avg:.3f} ms "
           f"(min {min(kernel_ms):.3f}, max {max(kernel_ms):.3f}); {achieved:.0f} GB/s",
           file=sys.stderr, flush=True)
+    # the same byte mix with trivial arithmetic, on the bench's own buffers
+    # (after the timed region: it overwrites the state)
+    import measure
+    ceil_gbps, ceil_cfg = measure.stream_ceiling(grads, [master, m, v], pout, S)
+    print(f"# same-mix streaming ceiling: {ceil_gbps:.0f} GB/s {ceil_cfg}", file=sys.stderr,
+          flush=True)
+    del grads
+    torch.cuda.empty_cache()
+    aux = [] if args.no_aux else aux_kernels(z, synth, workloads)
+    for a in aux:
+        print(f"# {a['kernel']}: {a['ms']:.3f} ms, {a['GBps']:.0f} GB/s", file=sys.stderr,
+              flush=True)
     cpu = None
     if not args.no_cpu_baseline:
-        del grads
-        torch.cuda.empty_cache()
         cpu = cpu_baseline(w, segs, S)
     out = {
         "metric": "shard-step elements/s and achieved HBM GB/s (% of MI355X peak), 1 GPU",
@@ -239,6 +312,11 @@ def main():
                      "kernel": "step_vec_kernel", "kernel_avg_ms": k_avg,
                      "algorithmic_bytes_per_launch": alg_bytes, "kernel_hash": kernel_hash()},
         "cpu_baseline": cpu,
+        "same_mix_ceiling": {"GBps": ceil_gbps, "frac_of_peak": ceil_gbps / PEAK_HBM_GBPS,
+                             "step_frac_of_ceiling": achieved / ceil_gbps,
+                             "kernel": "measure/stream_ceiling.hip: the step's bytes, "
+                                       "trivial arithmetic", "best_config": ceil_cfg},
+        "aux_kernels": aux,
     }
     print(json.dumps(out), flush=True)
 

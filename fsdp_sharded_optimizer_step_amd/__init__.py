@@ -6,8 +6,10 @@ exposes it to Python.
 """
 from .binding import (ACC_EMIT_BF16, ACC_NO_STORE, ACC_OVERWRITE, GRAD_COMPACT, GRAD_FLAT,
                       OUT_AG_SLOT, OUT_SHARD, AdamW, Layout, ZeroError, load, zero_bucket_pack,
-                      zero_grad_accumulate, zero_shard_step, zero_step_scalars)
+                      zero_gather_params, zero_grad_accumulate, zero_reshard, zero_shard_step,
+                      zero_step_scalars)
 
 __all__ = ["ACC_EMIT_BF16", "ACC_NO_STORE", "ACC_OVERWRITE", "GRAD_COMPACT", "GRAD_FLAT",
            "OUT_AG_SLOT", "OUT_SHARD", "AdamW", "Layout", "ZeroError", "load",
-           "zero_bucket_pack", "zero_grad_accumulate", "zero_shard_step", "zero_step_scalars"]
+           "zero_bucket_pack", "zero_gather_params", "zero_grad_accumulate", "zero_reshard",
+           "zero_shard_step", "zero_step_scalars"]

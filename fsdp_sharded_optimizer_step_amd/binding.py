@@ -24,7 +24,8 @@ ACC_OVERWRITE, ACC_EMIT_BF16, ACC_NO_STORE = 1, 2, 4
 EXPORTS = ("zero_layout_create", "zero_layout_destroy", "zero_layout_psi", "zero_layout_padded",
            "zero_layout_shard", "zero_layout_n_buckets", "zero_layout_n_d", "zero_layout_rank",
            "zero_layout_bucket", "zero_layout_tensor", "zero_bucket_pack", "zero_grad_accumulate",
-           "zero_shard_step", "zero_shard_step_ex", "zero_step_scalars", "zero_strerror")
+           "zero_shard_step", "zero_shard_step_ex", "zero_step_scalars", "zero_strerror",
+           "zero_gather_params", "zero_reshard")
 
 
 class ZeroError(RuntimeError):
@@ -38,8 +39,12 @@ class _AdamW(C.Structure):
                 ("eps", C.c_double), ("weight_decay", C.c_double)]
 
 
-class _Launch(C.Structure):
-    _fields_ = [("blocks", C.c_int32), ("threads", C.c_int32), ("path", C.c_int32)]
+DTYPE_BF16, DTYPE_F32 = 0, 1
+
+
+class _Options(C.Structure):
+    _fields_ = [("grad_dtype", C.c_int32), ("blocks", C.c_int32), ("threads", C.c_int32),
+                ("path", C.c_int32)]
 
 
 _lib = None
@@ -75,7 +80,9 @@ def load():
                                     vp, vp, vp, vp, C.c_int32, vp, vp]
     lib.zero_shard_step_ex.argtypes = [vp, C.POINTER(_AdamW), C.c_int64, C.POINTER(vp),
                                        C.c_int32, vp, vp, vp, vp, C.c_int32, vp,
-                                       C.POINTER(_Launch), vp]
+                                       C.POINTER(_Options), vp]
+    lib.zero_gather_params.argtypes = [vp, C.POINTER(vp), C.c_int64, C.c_int64, vp, vp]
+    lib.zero_reshard.argtypes = [vp, C.POINTER(vp), vp, vp, C.c_int32, vp]
     lib.zero_step_scalars.argtypes = [C.POINTER(_AdamW), C.c_int64, C.POINTER(C.c_float)]
     lib.zero_strerror.argtypes = [C.c_int]
     lib.zero_strerror.restype = C.c_char_p
@@ -175,10 +182,11 @@ def _dev32(t, name):
     return C.c_void_p(t.data_ptr())
 
 
-def _ptr_array(tensors, name):
+def _ptr_array(tensors, name, check=None):
+    check = check or _dev16
     arr = (C.c_void_p * max(1, len(tensors)))()
     for k, t in enumerate(tensors):
-        arr[k] = None if t is None else _dev16(t, f"{name}[{k}]").value
+        arr[k] = None if t is None else check(t, f"{name}[{k}]").value
     return arr
 
 
@@ -203,19 +211,48 @@ def zero_grad_accumulate(acc, grad, scale: float, flags: int = 0, bf16_out=None,
 def zero_shard_step(layout: Layout, hp: AdamW, t: int, rank_grads, grad_layout: int, master,
                     exp_avg, exp_avg_sq, param_out, out_mode: int, reduced_grad_out=None,
                     stream=None, launch=None):
-    """One shard step; `launch` = (blocks, threads, path) selects the launch
-    shape (zero_shard_step_ex)."""
+    """One shard step.  bf16 contributions (16-bit tensors) go through
+    zero_shard_step; float32 contributions, or an explicit launch shape
+    `launch` = (blocks, threads, path), through zero_shard_step_ex."""
+    import torch
     if len(rank_grads) != layout.n_d:
         raise ValueError("zero_shard_step: one contribution per rank is required")
-    args = [layout.handle, C.byref(hp._c()), int(t), _ptr_array(rank_grads, "rank_grads"),
-            grad_layout, _dev32(master, "master"), _dev32(exp_avg, "exp_avg"),
+    f32 = len(rank_grads) > 0 and rank_grads[0] is not None and rank_grads[0].dtype == torch.float32
+    grads = _ptr_array(rank_grads, "rank_grads", _dev32 if f32 else _dev16)
+    args = [layout.handle, C.byref(hp._c()), int(t), grads, grad_layout,
+            _dev32(master, "master"), _dev32(exp_avg, "exp_avg"),
             _dev32(exp_avg_sq, "exp_avg_sq"), _dev16(param_out, "param_out"), out_mode,
             _dev32(reduced_grad_out, "reduced_grad_out")]
-    if launch is None:
+    if launch is None and not f32:
         _check("zero_shard_step", load().zero_shard_step(*args, _stream_ptr(stream)))
     else:
-        _check("zero_shard_step_ex", load().zero_shard_step_ex(
-            *args, C.byref(_Launch(*launch)), _stream_ptr(stream)))
+        blocks, threads, path = launch if launch is not None else (0, 0, 0)
+        opt = _Options(DTYPE_F32 if f32 else DTYPE_BF16, blocks, threads, path)
+        _check("zero_shard_step_ex", load().zero_shard_step_ex(*args, C.byref(opt),
+                                                                _stream_ptr(stream)))
+
+
+def zero_gather_params(layout: Layout, rank_shards, full_out, bucket_begin: int = 0,
+                       bucket_end: int | None = None, stream=None):
+    if len(rank_shards) != layout.n_d:
+        raise ValueError("zero_gather_params: one shard per rank is required")
+    end = layout.n_buckets if bucket_end is None else bucket_end
+    _check("zero_gather_params", load().zero_gather_params(
+        layout.handle, _ptr_array(rank_shards, "rank_shards"), bucket_begin, end,
+        _dev16(full_out, "full_out"), _stream_ptr(stream)))
+
+
+def zero_reshard(src: Layout, src_shards, dst: Layout, dst_shard, stream=None):
+    """Re-cut one per-element array (float32 or 16-bit tensors) from src's
+    shards to dst's shard."""
+    import torch
+    if len(src_shards) != src.n_d:
+        raise ValueError("zero_reshard: one shard per source rank is required")
+    f32 = dst_shard.dtype == torch.float32
+    chk = _dev32 if f32 else _dev16
+    _check("zero_reshard", load().zero_reshard(
+        src.handle, _ptr_array(src_shards, "src_shards", chk), dst.handle,
+        chk(dst_shard, "dst_shard"), 4 if f32 else 2, _stream_ptr(stream)))
 
 
 def zero_step_scalars(hp: AdamW, t: int):

@@ -44,9 +44,12 @@ struct Region {
   int64_t i0, n0, n, seg, pstride, flat0, flat1;
 };
 
+// Contribution element type: GT_BF16 (2-byte patterns) or GT_F32.
+enum : int { GT_BF16 = 0, GT_F32 = 1 };
+
 template <int NP>
 struct StepArgs {
-  const uint16_t* g[NP];
+  const void* g[NP];
   float* master;
   float* m;
   float* v;
@@ -79,42 +82,82 @@ __device__ __forceinline__ void adamw(float g, float& th, float& m, float& v, co
   v = v1;
 }
 
-__device__ __forceinline__ void widen8(float a[8], const u32x4 w) {
-  a[0] = bf16_lo(w.x); a[1] = bf16_hi(w.x);
-  a[2] = bf16_lo(w.y); a[3] = bf16_hi(w.y);
-  a[4] = bf16_lo(w.z); a[5] = bf16_hi(w.z);
-  a[6] = bf16_lo(w.w); a[7] = bf16_hi(w.w);
+// 8 consecutive contributions of one rank, as loaded (not yet widened).
+template <int GT>
+struct Raw8;
+template <>
+struct Raw8<GT_BF16> {
+  u32x4 w;
+};
+template <>
+struct Raw8<GT_F32> {
+  f32x4 lo, hi;
+};
+
+template <int GT, bool NT>
+__device__ __forceinline__ Raw8<GT> load8(const void* base, int64_t gi) {
+  Raw8<GT> r;
+  if constexpr (GT == GT_BF16) {
+    r.w = ld_stream<NT>((const u32x4*)((const uint16_t*)base + gi));
+  } else {
+    r.lo = ld_stream<NT>((const f32x4*)((const float*)base + gi));
+    r.hi = ld_stream<NT>((const f32x4*)((const float*)base + gi + 4));
+  }
+  return r;
 }
 
-__device__ __forceinline__ void add8(float a[8], const u32x4 w) {
-  a[0] = a[0] + bf16_lo(w.x); a[1] = a[1] + bf16_hi(w.x);
-  a[2] = a[2] + bf16_lo(w.y); a[3] = a[3] + bf16_hi(w.y);
-  a[4] = a[4] + bf16_lo(w.z); a[5] = a[5] + bf16_hi(w.z);
-  a[6] = a[6] + bf16_lo(w.w); a[7] = a[7] + bf16_hi(w.w);
+template <int GT>
+__device__ __forceinline__ void widen8(float a[8], const Raw8<GT>& r) {
+  if constexpr (GT == GT_BF16) {
+    a[0] = bf16_lo(r.w.x); a[1] = bf16_hi(r.w.x);
+    a[2] = bf16_lo(r.w.y); a[3] = bf16_hi(r.w.y);
+    a[4] = bf16_lo(r.w.z); a[5] = bf16_hi(r.w.z);
+    a[6] = bf16_lo(r.w.w); a[7] = bf16_hi(r.w.w);
+  } else {
+    a[0] = r.lo.x; a[1] = r.lo.y; a[2] = r.lo.z; a[3] = r.lo.w;
+    a[4] = r.hi.x; a[5] = r.hi.y; a[6] = r.hi.z; a[7] = r.hi.w;
+  }
+}
+
+template <int GT>
+__device__ __forceinline__ void add8(float a[8], const Raw8<GT>& r) {
+  float x[8];
+  widen8<GT>(x, r);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a[k] = a[k] + x[k];
+}
+
+template <int GT>
+__device__ __forceinline__ float load_one(const void* base, int64_t gi) {
+  if constexpr (GT == GT_BF16)
+    return bf16_one(((const uint16_t*)base)[gi]);
+  else
+    return ((const float*)base)[gi];
 }
 
 // Sum of the N_d contributions of 8 consecutive elements, ascending rank.
-template <int ND, int GROUP, bool NT>
+// The loads of up to GROUP ranks are issued before their adds.
+template <int ND, int GROUP, bool NT, int GT>
 __device__ __forceinline__ void reduce8(float acc[8], const StepArgs<ND>& A, int64_t gi) {
-  widen8(acc, ld_stream<NT>((const u32x4*)(A.g[0] + gi)));
+  widen8<GT>(acc, load8<GT, NT>(A.g[0], gi));
 #pragma unroll
   for (int q0 = 1; q0 < ND; q0 += GROUP) {
-    u32x4 w[GROUP];
+    Raw8<GT> w[GROUP];
 #pragma unroll
     for (int u = 0; u < GROUP; ++u)
-      if (q0 + u < ND) w[u] = ld_stream<NT>((const u32x4*)(A.g[q0 + u] + gi));
+      if (q0 + u < ND) w[u] = load8<GT, NT>(A.g[q0 + u], gi);
 #pragma unroll
     for (int u = 0; u < GROUP; ++u)
-      if (q0 + u < ND) add8(acc, w[u]);
+      if (q0 + u < ND) add8<GT>(acc, w[u]);
   }
 }
 
 // Runtime rank count (any N_d up to ZERO_MAX_ND).
-template <bool NT>
+template <bool NT, int GT>
 __device__ __forceinline__ void reduce8_dyn(float acc[8], const StepArgs<ZERO_MAX_ND>& A,
                                             int64_t gi) {
-  widen8(acc, ld_stream<NT>((const u32x4*)(A.g[0] + gi)));
-  for (int q = 1; q < A.nd; ++q) add8(acc, ld_stream<NT>((const u32x4*)(A.g[q] + gi)));
+  widen8<GT>(acc, load8<GT, NT>(A.g[0], gi));
+  for (int q = 1; q < A.nd; ++q) add8<GT>(acc, load8<GT, NT>(A.g[q], gi));
 }
 
 __device__ __forceinline__ int64_t flat_of(const Region& r, int64_t e) {
@@ -124,14 +167,14 @@ __device__ __forceinline__ int64_t flat_of(const Region& r, int64_t e) {
 }
 
 // One element with generic addressing (tails, the scalar path).
-template <int NP>
+template <int GT, int NP>
 __device__ __forceinline__ void step_one(const StepArgs<NP>& A, int64_t e, bool map) {
   const int64_t i = A.reg.i0 + e;
   const int64_t f = map ? flat_of(A.reg, e) : i;
   const int64_t gi = (map && A.flat_grad) ? f : i;
   const int64_t oi = (map && A.slot_out) ? f : i;
-  float a = bf16_one(A.g[0][gi]);
-  for (int q = 1; q < A.nd; ++q) a = a + bf16_one(A.g[q][gi]);
+  float a = load_one<GT>(A.g[0], gi);
+  for (int q = 1; q < A.nd; ++q) a = a + load_one<GT>(A.g[q], gi);
   const float g = average<0>(a, A);
   float th = A.master[i], m = A.m[i], v = A.v[i];
   adamw(g, th, m, v, A.k);
@@ -150,7 +193,7 @@ __device__ __forceinline__ void step_one(const StepArgs<NP>& A, int64_t e, bool 
 template <int ND>
 using ArgsFor = StepArgs<(ND > 0 ? ND : ZERO_MAX_ND)>;
 
-template <int ND, bool MAP, int GROUP, bool NT>
+template <int ND, bool MAP, int GROUP, bool NT, int GT>
 __global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND> A) {
   const int64_t n = A.reg.n;
   const int64_t nv0 = A.reg.n0 >> 3;
@@ -184,9 +227,9 @@ __global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND> A) {
 
     float acc[8];
     if constexpr (ND > 0)
-      reduce8<ND, GROUP, NT>(acc, A, gi);
+      reduce8<ND, GROUP, NT, GT>(acc, A, gi);
     else
-      reduce8_dyn<NT>(acc, A, gi);
+      reduce8_dyn<NT, GT>(acc, A, gi);
 
     const f32x4 th0 = ld_stream<NT>((const f32x4*)(A.master + i));
     const f32x4 th1 = ld_stream<NT>((const f32x4*)(A.master + i + 4));
@@ -219,20 +262,21 @@ __global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND> A) {
   }
   // the elements after the last full vector, one per lane
   const int64_t tail0 = (nvec == nv0) ? (nv0 << 3) : A.reg.n0 + ((nvec - nv0) << 3);
-  if (tid < n - tail0) step_one(A, tail0 + tid, MAP);
+  if (tid < n - tail0) step_one<GT>(A, tail0 + tid, MAP);
 }
 
+template <int GT>
 __global__ void __launch_bounds__(256) step_scalar_kernel(const StepArgs<ZERO_MAX_ND> A, int map) {
   const int64_t n = A.reg.n;
   const int64_t T = (int64_t)gridDim.x * blockDim.x;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += T)
-    step_one(A, e, map != 0);
+    step_one<GT>(A, e, map != 0);
 }
 
 // ------------------------------------------------------------------ host
 struct Call {
-  const uint16_t* const* g;
-  int32_t nd;
+  const void* const* g;
+  int32_t nd, gt;
   float *master, *m, *v, *gout;
   uint16_t* pout;
   Scalars k;
@@ -271,50 +315,62 @@ int cu_count() {
 
 constexpr int kDefaultThreads = 256;
 
-// Launch policy, from measurements on MI355X (see the design notes): the
-// read-dominated large-N_d step streams best with non-temporal accesses and
-// one 256-thread block per CU; the small-N_d step (one third writes) with
-// ordinary accesses and two blocks per CU.
-constexpr bool nt_for(int nd) { return nd >= 32; }
-int default_blocks_per_cu(int nd) { return nd >= 32 ? 1 : 2; }
+// Launch policy, from measurements on MI355X: the read-dominated step
+// (64 or more bytes of contributions per element) streams best with
+// non-temporal accesses and one 256-thread block per CU; the step with a
+// larger write share (small N_d) with ordinary accesses and two blocks per CU.
+constexpr bool read_dominated(int nd, int gt) { return nd * (gt == GT_F32 ? 4 : 2) >= 64; }
+int default_blocks_per_cu(int nd, int gt) { return read_dominated(nd, gt) ? 1 : 2; }
 
-template <int ND, bool MAP>
+template <int ND, bool MAP, int GT>
 int launch_vec(const Call& c, const Region& reg, int blocks, int threads, hipStream_t s) {
   StepArgs<ND> A;
   fill_args(A, c, reg);
   constexpr int GROUP = (ND > 16) ? 16 : (ND > 1 ? ND - 1 : 1);
-  hipLaunchKernelGGL((step_vec_kernel<ND, MAP, GROUP, nt_for(ND)>), dim3(blocks), dim3(threads), 0,
-                     s, A);
+  hipLaunchKernelGGL((step_vec_kernel<ND, MAP, GROUP, read_dominated(ND, GT), GT>), dim3(blocks),
+                     dim3(threads), 0, s, A);
   return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
+}
+
+template <bool MAP, int GT>
+int dispatch_vec_gt(const Call& c, const Region& reg, int blocks, int threads, hipStream_t s) {
+  switch (c.nd) {
+    case 2: return launch_vec<2, MAP, GT>(c, reg, blocks, threads, s);
+    case 4: return launch_vec<4, MAP, GT>(c, reg, blocks, threads, s);
+    case 8: return launch_vec<8, MAP, GT>(c, reg, blocks, threads, s);
+    case 16: return launch_vec<16, MAP, GT>(c, reg, blocks, threads, s);
+    case 32: return launch_vec<32, MAP, GT>(c, reg, blocks, threads, s);
+    case 64: return launch_vec<64, MAP, GT>(c, reg, blocks, threads, s);
+    default: {
+      StepArgs<ZERO_MAX_ND> A;
+      fill_args(A, c, reg);
+      if (read_dominated(c.nd, GT))
+        hipLaunchKernelGGL((step_vec_kernel<0, MAP, 1, true, GT>), dim3(blocks), dim3(threads), 0,
+                           s, A);
+      else
+        hipLaunchKernelGGL((step_vec_kernel<0, MAP, 1, false, GT>), dim3(blocks), dim3(threads), 0,
+                           s, A);
+      return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
+    }
+  }
 }
 
 template <bool MAP>
 int dispatch_vec(const Call& c, const Region& reg, int blocks, int threads, hipStream_t s) {
-  switch (c.nd) {
-    case 2: return launch_vec<2, MAP>(c, reg, blocks, threads, s);
-    case 4: return launch_vec<4, MAP>(c, reg, blocks, threads, s);
-    case 8: return launch_vec<8, MAP>(c, reg, blocks, threads, s);
-    case 16: return launch_vec<16, MAP>(c, reg, blocks, threads, s);
-    case 32: return launch_vec<32, MAP>(c, reg, blocks, threads, s);
-    case 64: return launch_vec<64, MAP>(c, reg, blocks, threads, s);
-    default: {
-      StepArgs<ZERO_MAX_ND> A;
-      fill_args(A, c, reg);
-      if (c.nd >= 32)
-        hipLaunchKernelGGL((step_vec_kernel<0, MAP, 1, true>), dim3(blocks), dim3(threads), 0, s, A);
-      else
-        hipLaunchKernelGGL((step_vec_kernel<0, MAP, 1, false>), dim3(blocks), dim3(threads), 0, s,
-                           A);
-      return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
-    }
-  }
+  return c.gt == GT_F32 ? dispatch_vec_gt<MAP, GT_F32>(c, reg, blocks, threads, s)
+                        : dispatch_vec_gt<MAP, GT_BF16>(c, reg, blocks, threads, s);
 }
 
 int launch_scalar(const Call& c, const Region& reg, bool map, int blocks, int threads,
                   hipStream_t s) {
   StepArgs<ZERO_MAX_ND> A;
   fill_args(A, c, reg);
-  hipLaunchKernelGGL(step_scalar_kernel, dim3(blocks), dim3(threads), 0, s, A, map ? 1 : 0);
+  if (c.gt == GT_F32)
+    hipLaunchKernelGGL(step_scalar_kernel<GT_F32>, dim3(blocks), dim3(threads), 0, s, A,
+                       map ? 1 : 0);
+  else
+    hipLaunchKernelGGL(step_scalar_kernel<GT_BF16>, dim3(blocks), dim3(threads), 0, s, A,
+                       map ? 1 : 0);
   return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
 }
 
@@ -363,17 +419,21 @@ int zero_step_scalars(const zero_adamw* hp, int64_t t, float out[8]) {
 }
 
 int zero_shard_step_ex(const zero_layout* L, const zero_adamw* hp, int64_t t,
-                       const uint16_t* const* rank_grads, int32_t grad_layout, float* master,
+                       const void* const* rank_grads, int32_t grad_layout, float* master,
                        float* exp_avg, float* exp_avg_sq, uint16_t* param_out, int32_t out_mode,
-                       float* reduced_grad_out, const zero_launch* launch, hipStream_t stream) {
+                       float* reduced_grad_out, const zero_step_options* opt,
+                       hipStream_t stream) {
   if (!L || !hp || !rank_grads || t < 1 || !hp_ok(*hp)) return ZERO_EINVAL;
   if (grad_layout != ZERO_GRAD_COMPACT && grad_layout != ZERO_GRAD_FLAT) return ZERO_EINVAL;
   if (out_mode != ZERO_OUT_AG_SLOT && out_mode != ZERO_OUT_SHARD) return ZERO_EINVAL;
-  int threads = kDefaultThreads, blocks_cap = 0, path = 0;
-  if (launch) {
-    if (launch->threads > 0) threads = launch->threads;
-    if (launch->blocks > 0) blocks_cap = launch->blocks;
-    path = launch->path;
+  int threads = kDefaultThreads, blocks_cap = 0, path = 0, gt = GT_BF16;
+  if (opt) {
+    if (opt->grad_dtype != ZERO_DTYPE_BF16 && opt->grad_dtype != ZERO_DTYPE_F32)
+      return ZERO_EINVAL;
+    gt = opt->grad_dtype == ZERO_DTYPE_F32 ? GT_F32 : GT_BF16;
+    if (opt->threads > 0) threads = opt->threads;
+    if (opt->blocks > 0) blocks_cap = opt->blocks;
+    path = opt->path;
     if (threads % 64 != 0 || threads > 256 || (path != 0 && path != 1)) return ZERO_EINVAL;
   }
   const int32_t nd = L->n_d;
@@ -384,7 +444,7 @@ int zero_shard_step_ex(const zero_layout* L, const zero_adamw* hp, int64_t t,
     if (!rank_grads[q]) return ZERO_EINVAL;
 
   // outputs must not overlap each other or any input
-  const int64_t gbytes = 2 * (grad_layout == ZERO_GRAD_FLAT ? P : S);
+  const int64_t gbytes = (gt == GT_F32 ? 4 : 2) * (grad_layout == ZERO_GRAD_FLAT ? P : S);
   const Span outs[5] = {span(master, 4 * S), span(exp_avg, 4 * S), span(exp_avg_sq, 4 * S),
                         span(param_out, 2 * (out_mode == ZERO_OUT_AG_SLOT ? P : S)),
                         span(reduced_grad_out, reduced_grad_out ? 4 * S : 0)};
@@ -398,6 +458,7 @@ int zero_shard_step_ex(const zero_layout* L, const zero_adamw* hp, int64_t t,
   Call c;
   c.g = rank_grads;
   c.nd = nd;
+  c.gt = gt;
   c.master = master;
   c.m = exp_avg;
   c.v = exp_avg_sq;
@@ -411,7 +472,7 @@ int zero_shard_step_ex(const zero_layout* L, const zero_adamw* hp, int64_t t,
   bool aligned = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) &&
                  aligned16(param_out) && (!reduced_grad_out || aligned16(reduced_grad_out));
   for (int32_t q = 0; q < nd; ++q) aligned = aligned && aligned16(rank_grads[q]);
-  const int cap = blocks_cap > 0 ? blocks_cap : cu_count() * default_blocks_per_cu(nd);
+  const int cap = blocks_cap > 0 ? blocks_cap : cu_count() * default_blocks_per_cu(nd, gt);
   const bool allow_vec = path == 0 && aligned;
 
   // Launch plan.  Without flat addressing the shard is one plain range.
@@ -473,8 +534,9 @@ int zero_shard_step(const zero_layout* L, const zero_adamw* hp, int64_t t,
                     const uint16_t* const* rank_grads, int32_t grad_layout, float* master,
                     float* exp_avg, float* exp_avg_sq, uint16_t* param_out, int32_t out_mode,
                     float* reduced_grad_out, hipStream_t stream) {
-  return zero_shard_step_ex(L, hp, t, rank_grads, grad_layout, master, exp_avg, exp_avg_sq,
-                            param_out, out_mode, reduced_grad_out, nullptr, stream);
+  return zero_shard_step_ex(L, hp, t, (const void* const*)rank_grads, grad_layout, master,
+                            exp_avg, exp_avg_sq, param_out, out_mode, reduced_grad_out, nullptr,
+                            stream);
 }
 
 }  // extern "C"

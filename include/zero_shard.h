@@ -193,22 +193,80 @@ int zero_shard_step(const zero_layout* layout, const zero_adamw* hp, int64_t t,
                     float* exp_avg_dev, float* exp_avg_sq_dev, uint16_t* param_out_dev,
                     int32_t out_mode, float* reduced_grad_out_dev, hipStream_t stream);
 
-/* Same as zero_shard_step with an explicit launch shape, for tuning and for
- * checking that results do not depend on it.  blocks <= 0 and threads <= 0
- * pick the defaults; threads must be a multiple of 64 and at most 1024;
- * path: 0 = automatic, 1 = force the scalar kernel.  Errors as above, plus
- * ZERO_EINVAL for a bad launch shape. */
+/* Same as zero_shard_step with options: the contributions' element type and
+ * the launch shape.
+ *
+ * grad_dtype ZERO_DTYPE_BF16: rank_grads_dev[q] points to bf16 values, as in
+ *   zero_shard_step.
+ * grad_dtype ZERO_DTYPE_F32: rank_grads_dev[q] points to binary32 values (a
+ *   Reduce-Scatter carried out in fp32, e.g. the ranks' no_sync fp32
+ *   accumulators handed over without rounding to bf16); the reduction is
+ *   a = G_0; a = a + G_q for q = 1..n_d-1, then the same update.  Reads
+ *   4*n_d + 26 bytes per shard element instead of 2*n_d + 26.
+ * blocks <= 0 and threads <= 0 pick the defaults; threads must be a multiple
+ * of 64 and at most 256; path 0 = automatic, 1 = force the scalar kernel.
+ * opt == NULL means {ZERO_DTYPE_BF16, 0, 0, 0}.  Results do not depend on
+ * blocks, threads or path.  Errors as for zero_shard_step, plus ZERO_EINVAL
+ * for a bad dtype or launch shape. */
+#define ZERO_DTYPE_BF16 0
+#define ZERO_DTYPE_F32 1
+
 typedef struct {
+  int32_t grad_dtype;
   int32_t blocks;
   int32_t threads;
   int32_t path;
-} zero_launch;
+} zero_step_options;
 
 int zero_shard_step_ex(const zero_layout* layout, const zero_adamw* hp, int64_t t,
-                       const uint16_t* const* rank_grads_dev, int32_t grad_layout,
+                       const void* const* rank_grads_dev, int32_t grad_layout,
                        float* master_dev, float* exp_avg_dev, float* exp_avg_sq_dev,
                        uint16_t* param_out_dev, int32_t out_mode, float* reduced_grad_out_dev,
-                       const zero_launch* launch, hipStream_t stream);
+                       const zero_step_options* opt, hipStream_t stream);
+
+/* --------------------------------------------------------- parameter gather
+ * ("Zero Redundancy Optimizer (ZeRO)": ZeRO-1/2 All-Gather the updated
+ * parameters after the step; ZeRO-3 All-Gathers each layer's parameters
+ * before forward and again before backward.)
+ *
+ * The local arithmetic of that All-Gather: for every bucket b in
+ * [bucket_begin, bucket_end) and every rank q, copy rank q's slice of b
+ * (S_b bf16 values at shard offset shard_off_b of rank_shards_dev[q]) to
+ * full_out_dev[padded_off_b + q*S_b ...].  Padding is copied as it is held
+ * by the shards (+0 when the shards were produced by zero_shard_step from
+ * zero-initialised padding).  Elements of full_out_dev outside the bucket
+ * range are not touched.
+ *
+ * rank_shards_dev: HOST array of n_d DEVICE pointers, each S bf16 values
+ * (a rank's shard in shard order, as zero_shard_step's ZERO_OUT_SHARD
+ * output).  full_out_dev: P bf16 values; must not overlap any shard.
+ * Moves 4 bytes per flat element.
+ * Errors: ZERO_EINVAL, ZERO_ERANGE (bucket range), ZERO_EOVERLAP, ZERO_EHIP. */
+int zero_gather_params(const zero_layout* layout, const uint16_t* const* rank_shards_dev,
+                       int64_t bucket_begin, int64_t bucket_end, uint16_t* full_out_dev,
+                       hipStream_t stream);
+
+/* ----------------------------------------------------------------- reshard
+ * ("Fully Sharded Data Parallel (FSDP)", "Checkpoint": every rank saves its
+ * own shards; loading re-cuts them for the target layout, including a
+ * different number of GPUs; optimizer state has to be saved and re-cut too.)
+ *
+ * Re-cut one per-element array (fp32 master / m / v, or bf16 parameters)
+ * from the n_d shards of layout `src` into the shard of layout `dst` (its
+ * own n_d' and rank): dst_shard_dev[i] = value of the parameter at stream
+ * position x(i) taken from the src shard that owns x(i); dst padding is
+ * written as 0.  Both layouts must describe the same tensor list (equal
+ * numel arrays); bucket capacity, n_d and rank may differ.
+ *
+ * src_shards_dev: HOST array of src's n_d DEVICE pointers, each src S values.
+ * dst_shard_dev: dst S values; must not overlap any source.
+ * elem_bytes: 4 (fp32 state) or 2 (bf16).  Moves 2*elem_bytes bytes per
+ * destination element.
+ * Errors: ZERO_EINVAL (null, bad elem_bytes, different tensor lists),
+ * ZERO_EOVERLAP, ZERO_EHIP. */
+int zero_reshard(const zero_layout* src, const void* const* src_shards_dev,
+                 const zero_layout* dst, void* dst_shard_dev, int32_t elem_bytes,
+                 hipStream_t stream);
 
 /* Per-call binary32 scalars for step t, in the order
  * {s, rho, a_wd, B1, C1, B2, C2, E}.  Errors: ZERO_EINVAL. */

@@ -1,0 +1,54 @@
+"""Measurement helpers for bench.py: the same-mix streaming ceiling."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmeasure.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("measure/libmeasure.so is not built (run __graft_entry__.build())")
+        lib = C.CDLL(_LIB_PATH)
+        lib.stream_ceiling_launch.argtypes = [C.POINTER(C.c_void_p), C.c_int32,
+                                              C.POINTER(C.c_void_p), C.c_void_p, C.c_int64,
+                                              C.c_int32, C.c_int32, C.c_void_p]
+        lib.stream_ceiling_launch.restype = C.c_int
+        _lib = lib
+    return _lib
+
+
+def stream_ceiling(grads, state, out, n: int, reps: int = 5):
+    """Best bandwidth (GB/s of 2*N_d + 26 bytes per element) of the same-mix
+    kernel over a few launch shapes, on the given (scratch) buffers."""
+    import torch
+    lib = _load()
+    nd = len(grads)
+    g = (C.c_void_p * nd)(*[t.data_ptr() for t in grads])
+    s = (C.c_void_p * 3)(*[t.data_ptr() for t in state])
+    n = n // 8 * 8
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    best = (0.0, None)
+    for bpc in (1, 2, 4):
+        for nt in (0, 1):
+            args = (g, nd, s, out.data_ptr(), n, cus * bpc, nt, stream.cuda_stream)
+            if lib.stream_ceiling_launch(*args) != 0:
+                raise RuntimeError("stream_ceiling_launch failed")
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                lib.stream_ceiling_launch(*args)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            gbps = n * (2 * nd + 26) / (ms * 1e-3) / 1e9
+            if gbps > best[0]:
+                best = (gbps, {"blocks_per_cu": bpc, "nontemporal": bool(nt), "ms": ms})
+    return best

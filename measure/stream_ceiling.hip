@@ -1,0 +1,98 @@
+// Same-mix streaming ceiling: a kernel that moves exactly the bytes of the
+// shard step (N_d 16-byte contribution loads, three in-place fp32 state
+// arrays read and written, one 16-byte bf16 store per 8 elements and lane)
+// with trivial integer arithmetic.  Its bandwidth is what the memory system
+// delivers for the step's access mix on this GPU; the step kernel is
+// reported as a fraction of it next to the fraction of the 8 TB/s peak.
+//
+// Measurement infrastructure only: not part of the update, not called by
+// the library.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kMaxRanks = 64;
+
+struct MixArgs {
+  const u32x4* g[kMaxRanks];  // N_d arrays of nvec 16-byte vectors
+  u32x4* s[3];                // 3 arrays of 2*nvec vectors, updated in place
+  u32x4* p;                   // nvec vectors
+  int64_t nvec;
+  int32_t nd;
+};
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void st(u32x4* p, u32x4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+template <int ND, bool NT>
+__global__ void __launch_bounds__(256) mix_kernel(const MixArgs a) {
+  const int64_t T = (int64_t)gridDim.x * blockDim.x;
+  const int nd = ND > 0 ? ND : a.nd;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < a.nvec; v += T) {
+    u32x4 acc = ld<NT>(a.g[0] + v);
+#pragma unroll
+    for (int q = 1; q < (ND > 0 ? ND : kMaxRanks); ++q)
+      if (q < nd) acc += ld<NT>(a.g[q] + v);
+    u32x4 x[6];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      x[2 * k] = ld<NT>(a.s[k] + 2 * v);
+      x[2 * k + 1] = ld<NT>(a.s[k] + 2 * v + 1);
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      st<NT>(a.s[k] + 2 * v, x[2 * k] + acc);
+      st<NT>(a.s[k] + 2 * v + 1, x[2 * k + 1] ^ acc);
+    }
+    st<NT>(a.p + v, acc);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+// grads: host array of nd device pointers to n bf16 values each; state: 3
+// device pointers to n floats; out: n bf16 values.  n must be a multiple of
+// 8 and every pointer 16-byte aligned.  Returns 0, -1 on bad arguments, -2
+// on a launch failure.
+int stream_ceiling_launch(const void* const* grads, int32_t nd, void* const* state, void* out,
+                          int64_t n, int32_t blocks, int32_t nt, hipStream_t stream) {
+  if (nd < 1 || nd > kMaxRanks || n < 0 || n % 8 != 0 || blocks < 1 || !grads || !state || !out)
+    return -1;
+  MixArgs a;
+  for (int q = 0; q < kMaxRanks; ++q) a.g[q] = q < nd ? (const u32x4*)grads[q] : nullptr;
+  for (int k = 0; k < 3; ++k) a.s[k] = (u32x4*)state[k];
+  a.p = (u32x4*)out;
+  a.nvec = n / 8;
+  a.nd = nd;
+  for (int q = 0; q < nd; ++q)
+    if (!grads[q] || ((uintptr_t)grads[q] & 15u)) return -1;
+  for (int k = 0; k < 3; ++k)
+    if (!state[k] || ((uintptr_t)state[k] & 15u)) return -1;
+  if ((uintptr_t)out & 15u) return -1;
+  if (nd == 8) {
+    if (nt) hipLaunchKernelGGL((mix_kernel<8, true>), dim3(blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((mix_kernel<8, false>), dim3(blocks), dim3(256), 0, stream, a);
+  } else if (nd == 64) {
+    if (nt) hipLaunchKernelGGL((mix_kernel<64, true>), dim3(blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((mix_kernel<64, false>), dim3(blocks), dim3(256), 0, stream, a);
+  } else {
+    if (nt) hipLaunchKernelGGL((mix_kernel<0, true>), dim3(blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((mix_kernel<0, false>), dim3(blocks), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+}  // extern "C"

@@ -45,6 +45,16 @@ def _load():
     lib.oracle_step_scalars.argtypes = [C.c_double] * 5 + [C.c_int64, _f32p]
     lib.oracle_shard_step.argtypes = [C.c_int32, C.POINTER(_u16p), C.c_int64] + [C.c_double] * 5 + [
         C.c_int64, _f32p, _f32p, _f32p, _u16p, _f32p, C.c_int32]
+    lib.oracle_shard_step_f32.argtypes = [C.c_int32, C.POINTER(_f32p), C.c_int64] + [
+        C.c_double] * 5 + [C.c_int64, _f32p, _f32p, _f32p, _u16p, _f32p, C.c_int32]
+    lib.oracle_shard_step_f32.restype = C.c_int
+    lib.oracle_gather.argtypes = [C.POINTER(_u16p), _i64p, C.c_int32, C.c_int64, C.c_int32, _u16p]
+    lib.oracle_plan_locate.argtypes = [_i64p, C.c_int32, C.c_int64, C.c_int32, _i64p, C.c_int64,
+                                       C.POINTER(C.c_int32), _i64p]
+    lib.oracle_reshard.argtypes = [C.POINTER(C.c_void_p), _i64p, C.c_int32, C.c_int64, C.c_int32,
+                                   C.c_int64, C.c_int32, C.c_int32, C.c_void_p, C.c_int32]
+    for name in ("oracle_gather", "oracle_plan_locate", "oracle_reshard"):
+        getattr(lib, name).restype = C.c_int
     lib.oracle_model_state_bytes.argtypes = [C.c_int32, C.c_int64, C.c_int64, C.c_int32]
     lib.oracle_model_state_bytes.restype = C.c_double
     for name in ("oracle_plan_counts", "oracle_plan_buckets", "oracle_plan_tensor_ranges",
@@ -154,6 +164,42 @@ def slice_shard(flat: np.ndarray, pl: Plan, rank: int) -> np.ndarray:
     return out
 
 
+def gather(shards, pl: Plan) -> np.ndarray:
+    """The N_d ranks' shards -> the padded flat buffer (local All-Gather)."""
+    ss = [np.ascontiguousarray(x, dtype=np.uint16).reshape(-1) for x in shards]
+    assert len(ss) == pl.n_d and all(x.size == pl.shard_len for x in ss)
+    arr = (_u16p * len(ss))(*[_ptr(x, C.c_uint16) for x in ss])
+    out = np.empty(pl.padded_total, np.uint16)
+    _check(_load().oracle_gather(arr, _ptr(pl.numel, C.c_int64), pl.numel.size, pl.cap, pl.n_d,
+                                 _ptr(out, C.c_uint16)), "gather")
+    return out
+
+
+def locate(pl: Plan, xs):
+    """stream positions -> (owning rank, index in its shard)"""
+    xs = _i64(xs)
+    r = np.empty(xs.size, np.int32)
+    i = np.empty(xs.size, np.int64)
+    _check(_load().oracle_plan_locate(_ptr(pl.numel, C.c_int64), pl.numel.size, pl.cap, pl.n_d,
+                                      _ptr(xs, C.c_int64), xs.size, _ptr(r, C.c_int32),
+                                      _ptr(i, C.c_int64)), "plan_locate")
+    return r, i
+
+
+def reshard(src_shards, src: Plan, dst: Plan, dst_rank: int) -> np.ndarray:
+    """Re-cut one per-element array from src's shards to dst's shard of rank dst_rank."""
+    ss = [np.ascontiguousarray(x) for x in src_shards]
+    dt = ss[0].dtype
+    assert dt in (np.float32, np.uint16) and all(x.dtype == dt for x in ss)
+    assert np.array_equal(src.numel, dst.numel) and len(ss) == src.n_d
+    arr = (C.c_void_p * len(ss))(*[x.ctypes.data for x in ss])
+    out = np.empty(dst.shard_len, dt)
+    _check(_load().oracle_reshard(arr, _ptr(src.numel, C.c_int64), src.numel.size, src.cap,
+                                  src.n_d, dst.cap, dst.n_d, dst_rank, out.ctypes.data,
+                                  dt.itemsize), "reshard")
+    return out
+
+
 # ----------------------------------------------------------------- accumulate
 def accumulate(acc: np.ndarray, g: np.ndarray, scale: float, overwrite: bool,
                store_acc: bool = True, emit: bool = False):
@@ -205,6 +251,26 @@ def shard_step(grads, master, m, v, hp: AdamW, t: int, want_grad: bool = False,
                                      _ptr(m, C.c_float), _ptr(v, C.c_float), _ptr(p, C.c_uint16),
                                      _ptr(g_out, C.c_float) if want_grad else None, nthreads),
            "shard_step")
+    return p, g_out
+
+
+def shard_step_f32(grads, master, m, v, hp: AdamW, t: int, want_grad: bool = False,
+                   nthreads: int = 1):
+    """As shard_step, with binary32 contributions."""
+    gs = [np.ascontiguousarray(g, dtype=np.float32).reshape(-1) for g in grads]
+    n = master.size
+    for a in (master, m, v):
+        assert a.dtype == np.float32 and a.flags["C_CONTIGUOUS"] and a.size == n
+    assert all(g.size == n for g in gs)
+    arr = (_f32p * len(gs))(*[_ptr(g, C.c_float) for g in gs])
+    p = np.empty(n, np.uint16)
+    g_out = np.empty(n, np.float32) if want_grad else None
+    _check(_load().oracle_shard_step_f32(len(gs), arr, n, hp.lr, hp.beta1, hp.beta2, hp.eps,
+                                         hp.weight_decay, t, _ptr(master, C.c_float),
+                                         _ptr(m, C.c_float), _ptr(v, C.c_float),
+                                         _ptr(p, C.c_uint16),
+                                         _ptr(g_out, C.c_float) if want_grad else None, nthreads),
+           "shard_step_f32")
     return p, g_out
 
 

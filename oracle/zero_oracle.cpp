@@ -171,12 +171,17 @@ Scalars make_scalars(double lr, double b1, double b2, double eps, double wd, int
   return k;
 }
 
-void step_range(int32_t n_d, const uint16_t* const* G, int64_t lo, int64_t hi, const Scalars& k,
+float contribution(const uint16_t* g, int64_t i) { return widen_bf16(g[i]); }
+float contribution(const float* g, int64_t i) { return g[i]; }
+
+// Contributions are bf16 patterns (uint16_t) or binary32 values (float).
+template <class T>
+void step_range(int32_t n_d, const T* const* G, int64_t lo, int64_t hi, const Scalars& k,
                 float* master, float* m, float* v, uint16_t* p_out, float* g_out) {
   const float nd = (float)n_d;
   for (int64_t i = lo; i < hi; ++i) {
-    float a = widen_bf16(G[0][i]);
-    for (int32_t q = 1; q < n_d; ++q) a = a + widen_bf16(G[q][i]);
+    float a = contribution(G[0], i);
+    for (int32_t q = 1; q < n_d; ++q) a = a + contribution(G[q], i);
     float g = a / nd;
     float m1 = k.B1 * m[i] + k.C1 * g;
     float v1 = k.B2 * v[i] + k.C2 * (g * g);
@@ -333,6 +338,79 @@ int oracle_slice(const uint16_t* flat, const int64_t* numel, int32_t n_tensors, 
   return 0;
 }
 
+// --- Parameter gather (local part of the All-Gather) ---------------------------
+// [DP] "Zero Redundancy Optimizer (ZeRO)": after the step (ZeRO-1/2) or per
+// layer before forward/backward (ZeRO-3) the ranks' parameter shards are
+// All-Gathered into the full flat buffer: rank q's slice of every bucket
+// goes back to slot q of that bucket.
+// Pinned by: gather(slices of x) == x for packed x (inverse of the pinned
+// slice), brute force on tiny layouts.
+int oracle_gather(const uint16_t* const* shards, const int64_t* numel, int32_t n_tensors,
+                  int64_t cap, int32_t n_d, uint16_t* out) {
+  if (!plan_args_ok(numel, n_tensors, n_d)) return -1;
+  Plan p = make_plan(numel, n_tensors, cap, n_d);
+  for (size_t b = 0; b < p.len.size(); ++b) {
+    int64_t sb = p.padded_len[b] / n_d;
+    for (int32_t q = 0; q < n_d; ++q)
+      for (int64_t j = 0; j < sb; ++j)
+        out[p.padded_off[b] + (int64_t)q * sb + j] = shards[q][p.shard_off[b] + j];
+  }
+  return 0;
+}
+
+// Stream positions -> (owning rank, index in that rank's shard).
+int oracle_plan_locate(const int64_t* numel, int32_t n_tensors, int64_t cap, int32_t n_d,
+                       const int64_t* xs, int64_t n, int32_t* rank, int64_t* idx) {
+  if (!plan_args_ok(numel, n_tensors, n_d)) return -1;
+  Plan p = make_plan(numel, n_tensors, cap, n_d);
+  for (int64_t k = 0; k < n; ++k) {
+    if (xs[k] < 0 || xs[k] >= p.total) return -1;
+    auto it = std::upper_bound(p.stream_off.begin(), p.stream_off.end(), xs[k]);
+    int64_t b = (int64_t)(it - p.stream_off.begin()) - 1;
+    int64_t sb = p.padded_len[b] / n_d;
+    int64_t w = xs[k] - p.stream_off[b];
+    rank[k] = (int32_t)(w / sb);
+    idx[k] = p.shard_off[b] + (w - (int64_t)rank[k] * sb);
+  }
+  return 0;
+}
+
+// --- Reshard between layouts (sharded checkpoint loaded with another N_d) ------
+// [DP] "Fully Sharded Data Parallel (FSDP)" / "Checkpoint": every rank saves
+// its shards; loading re-cuts them for the target sharding layout, which may
+// use a different number of GPUs; optimizer state is saved and re-cut too.
+// dst[i] = the value of the parameter at stream position x(i) in the source
+// shards, 0 at destination padding.  elem_bytes is 2 or 4.
+// Pinned by: identity on the same layout, A->B->A round trip, labelled
+// elements landing at the brute-force planner's positions.
+int oracle_reshard(const void* const* src, const int64_t* numel, int32_t n_tensors,
+                   int64_t src_cap, int32_t src_nd, int64_t dst_cap, int32_t dst_nd,
+                   int32_t dst_rank, void* dst, int32_t elem_bytes) {
+  if (!plan_args_ok(numel, n_tensors, src_nd) || !plan_args_ok(numel, n_tensors, dst_nd)) return -1;
+  if (dst_rank < 0 || dst_rank >= dst_nd || (elem_bytes != 2 && elem_bytes != 4)) return -1;
+  Plan ps = make_plan(numel, n_tensors, src_cap, src_nd);
+  Plan pd = make_plan(numel, n_tensors, dst_cap, dst_nd);
+  for (int64_t i = 0; i < pd.shard_len; ++i) {
+    int64_t b = bucket_of_shard_index(pd, i);
+    int64_t sb = pd.padded_len[b] / dst_nd;
+    int64_t pos = (int64_t)dst_rank * sb + (i - pd.shard_off[b]);
+    char* d = (char*)dst + i * elem_bytes;
+    if (pos >= pd.len[b]) {
+      std::memset(d, 0, elem_bytes);
+      continue;
+    }
+    int64_t x = pd.stream_off[b] + pos;
+    auto it = std::upper_bound(ps.stream_off.begin(), ps.stream_off.end(), x);
+    int64_t bs = (int64_t)(it - ps.stream_off.begin()) - 1;
+    int64_t ss = ps.padded_len[bs] / src_nd;
+    int64_t w = x - ps.stream_off[bs];
+    int64_t q = w / ss;
+    int64_t j = ps.shard_off[bs] + (w - q * ss);
+    std::memcpy(d, (const char*)src[q] + j * elem_bytes, elem_bytes);
+  }
+  return 0;
+}
+
 // --- no_sync gradient accumulation -------------------------------------------
 // [DP] "Naive Data Parallelism": gradients of several micro-batches are summed
 // locally and only the last one is synchronised; with n equal micro-batches
@@ -371,6 +449,23 @@ void oracle_step_scalars(double lr, double b1, double b2, double eps, double wd,
 int oracle_shard_step(int32_t n_d, const uint16_t* const* G, int64_t n, double lr, double b1,
                       double b2, double eps, double wd, int64_t t, float* master, float* m,
                       float* v, uint16_t* p_out, float* g_out, int32_t nthreads) {
+  if (n_d < 1 || n < 0 || t < 1 || !G) return -1;
+  for (int32_t q = 0; q < n_d; ++q)
+    if (!G[q] && n > 0) return -1;
+  Scalars k = make_scalars(lr, b1, b2, eps, wd, t);
+  parallel_chunks(n, nthreads, [&](int64_t lo, int64_t hi) {
+    step_range(n_d, G, lo, hi, k, master, m, v, p_out, g_out);
+  });
+  return 0;
+}
+
+// Same update with binary32 contributions (a Reduce-Scatter carried out in
+// fp32): a = G_0; a = a + G_q in ascending rank order; then as above.
+// Pinned by: equality with oracle_shard_step when every contribution is a
+// bf16 value, plus the rank-order and exact-sum cases in fp32.
+int oracle_shard_step_f32(int32_t n_d, const float* const* G, int64_t n, double lr, double b1,
+                          double b2, double eps, double wd, int64_t t, float* master, float* m,
+                          float* v, uint16_t* p_out, float* g_out, int32_t nthreads) {
   if (n_d < 1 || n < 0 || t < 1 || !G) return -1;
   for (int32_t q = 0; q < n_d; ++q)
     if (!G[q] && n > 0) return -1;

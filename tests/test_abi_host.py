@@ -149,10 +149,20 @@ def test_step_argument_errors_before_launch():
     assert step(grads=(C.c_void_p * 2)(0x100000, 0x400000 + 4)) == E.ZERO_EOVERLAP
     assert step(gout=0x600000 + 8) == E.ZERO_EOVERLAP
     # bad launch shapes
-    bad = binding._Launch(0, 100, 0)
+    bad = binding._Options(0, 0, 100, 0)
     rc = lib.zero_shard_step_ex(L.handle, C.byref(hp), 1, g, 0, 0x300000, 0x400000, 0x500000,
                                 0x600000, 1, None, C.byref(bad), None)
     assert rc == E.ZERO_EINVAL
+    bad_dtype = binding._Options(7, 0, 0, 0)
+    rc = lib.zero_shard_step_ex(L.handle, C.byref(hp), 1, g, 0, 0x300000, 0x400000, 0x500000,
+                                0x600000, 1, None, C.byref(bad_dtype), None)
+    assert rc == E.ZERO_EINVAL
+    # S = 32: 64 bytes of bf16 end just before master, 128 bytes of fp32 reach into it
+    g2 = (C.c_void_p * 2)(0x300000 - 64, 0x200000)
+    f32opt = binding._Options(1, 0, 0, 0)
+    rc = lib.zero_shard_step_ex(L.handle, C.byref(hp), 1, g2, 0, 0x300000, 0x400000, 0x500000,
+                                0x600000, 1, None, C.byref(f32opt), None)
+    assert rc == E.ZERO_EOVERLAP
     # empty shard: nothing to do, succeeds without touching the GPU
     L0 = z.Layout([], 0, 2, 0)
     assert step(layout=L0.handle) == E.ZERO_OK

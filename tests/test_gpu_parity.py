@@ -444,3 +444,218 @@ def test_gpu_bf16_cast_exhaustive():
             gn = got[nan].astype(np.uint32)
             assert (((gn & 0x7F80) == 0x7F80) & ((gn & 0x7F) != 0)).all()
             say(f"  cast chunk {c} ok")
+
+
+# ------------------------------------------------------------------ fp32 contributions
+F32_EDGE = [
+    ([1000, 37, 4096, 3], 1500, 4, 3, "flat", "ag_slot"),
+    ([17], 0, 1, 0, "compact", "shard"),
+    ([5, 0, 123, 64], 40, 3, 2, "flat", "ag_slot"),
+    ([70000, 3], 16384, 8, 7, "flat", "ag_slot"),
+    ([50000], 8008, 8, 3, "compact", "ag_slot"),
+    ([20000, 20001], 0, 16, 15, "compact", "shard"),
+    ([64 * 300 + 1], 6400, 64, 63, "compact", "shard"),
+    ([100 * 97], 0, 100, 99, "flat", "ag_slot"),
+]
+
+
+def _f32_contribs(case, t, flat):
+    """fp32 contributions keyed like the bf16 ones; FLAT ones laid out over
+    the padded flat buffer of each rank."""
+    w = case.w
+    pl = case.pl
+    if flat:
+        segs = [(int(po), int(so), int(ln), int(pln - ln))
+                for so, ln, po, pln in zip(pl.stream_off, pl.len, pl.padded_off, pl.padded_len)]
+        n = case.P
+    else:
+        segs, n = case.segs, case.S
+    dev, host = [], []
+    for q in range(w.n_d):
+        k = synth.key(w.name, "grad", q, 0, t)
+        g = torch.empty(n, dtype=torch.float32, device=DEV)
+        synth.fill_device(g, segs, k, *w.grad)
+        dev.append(g)
+        host.append(synth.values_at(case.stream_pos, k, *w.grad, synth.OUT_F32))
+    return dev, host
+
+
+@pytest.mark.parametrize("numel,cap,n_d,rank,gl,om", F32_EDGE)
+def test_f32_contributions_full_compare(numel, cap, n_d, rank, gl, om):
+    case = _edge_case(numel, cap, n_d, rank, gl, om)
+    say(f"  f32 numel={numel} cap={cap} n_d={n_d} r={rank} {gl} {om}: S={case.S}")
+    case.init_state_gpu()
+    case.init_state_oracle()
+    for t in (1, 2, 3):
+        dev, host = _f32_contribs(case, t, gl == "flat")
+        case.step_gpu(t, dev)
+        p, g = oracle.shard_step_f32(host, case.o_master, case.o_m, case.o_v, case.hp_o, t,
+                                     want_grad=True)
+        case.o_p, case.o_g = p, g
+    torch.cuda.synchronize()
+    case.compare("f32")
+    for a, b in ((case.master, case.o_master), (case.m, case.o_m), (case.v, case.o_v)):
+        assert_bitwise(a.cpu().numpy(), b, "state")
+    case.check_canaries(n_probe=4096)
+
+
+@pytest.mark.parametrize("launch", [(3, 64, 0), (0, 0, 1), (5000, 256, 0)])
+def test_f32_launch_shape_invariance(launch):
+    outs = []
+    for lc in (None, launch):
+        case = _edge_case([200_003, 77], 65_536, 16, 9, "flat", "ag_slot")
+        case.init_state_gpu()
+        dev, _ = _f32_contribs(case, 4, True)
+        case.step_gpu(4, dev, launch=lc)
+        torch.cuda.synchronize()
+        outs.append([case.master.cpu().numpy(), u16(case.pout), case.gout.cpu().numpy()])
+    for a, b in zip(*outs):
+        assert_bitwise(a, b, f"f32 launch {launch}")
+
+
+def test_no_sync_fp32_accumulators_feed_the_step():
+    """Each rank's 4 micro-batches accumulate into fp32 (scaled by 1/4); the
+    fp32 accumulators go to the step unrounded (fp32 Reduce-Scatter)."""
+    w = workloads.Workload("flat1m", [3_000_001], 0, 8, 5, "compact", "ag_slot", 101, 1,
+                           ("zero", 0.0), ("normal", 0.02), ("normal", 1e-4),
+                           ("absnormal", 1e-6), n_micro=4, micro_grad=("normal", 2e-3))
+    case = Case(w)
+    case.init_state_gpu()
+    case.init_state_oracle()
+    accs, o_accs = [], []
+    for q in range(w.n_d):
+        acc = torch.empty(case.S, dtype=torch.float32, device=DEV)
+        o_acc = np.zeros(case.S, np.float32)
+        micro = torch.empty(case.S, dtype=torch.int16, device=DEV)
+        for k in range(w.n_micro):
+            key = synth.key(w.name, "micro_grad", q, k, w.t_first)
+            synth.fill_device(micro, case.segs, key, *w.micro_grad)
+            z.zero_grad_accumulate(acc, micro, 0.25, z.ACC_OVERWRITE if k == 0 else 0)
+            oracle.accumulate(o_acc, synth.values_at(case.stream_pos, key, *w.micro_grad,
+                                                      synth.OUT_BF16), 0.25, overwrite=(k == 0))
+        accs.append(acc)
+        o_accs.append(o_acc)
+    case.step_gpu(w.t_first, accs)
+    p, g = oracle.shard_step_f32(o_accs, case.o_master, case.o_m, case.o_v, case.hp_o, w.t_first,
+                                 want_grad=True)
+    case.o_p, case.o_g = p, g
+    torch.cuda.synchronize()
+    for a, b in zip(accs, o_accs):
+        assert_bitwise(a.cpu().numpy(), b, "fp32 accumulator")
+    case.compare("fp32 no_sync")
+    assert_bitwise(case.master.cpu().numpy(), case.o_master, "master")
+
+
+# ------------------------------------------------------------------ gather / reshard
+GATHER = [
+    ([1000, 37, 4096, 3], 1500, 4),
+    ([5, 0, 123, 64], 40, 3),
+    ([50000], 8008, 8),           # slice 1001: scalar path
+    ([70000, 3], 16384, 8),       # vector path, short last bucket
+    ([64 * 300 + 1], 6400, 64),
+    ([256 * 33 + 7], 0, 256),
+]
+
+
+def _rank_shards_bf16(pl, n_d, seed):
+    out_h = []
+    for q in range(n_d):
+        segs = synth.shard_segments(pl.stream_off, pl.len, pl.padded_len, pl.shard_off, n_d, q)
+        out_h.append(synth.fill_host(pl.shard_len, synth.OUT_BF16, segs,
+                                     synth.key("gpt2s", "master", q, 0, seed), "normal", 0.02))
+    return out_h
+
+
+@pytest.mark.parametrize("numel,cap,n_d", GATHER)
+def test_gather_params_matches_oracle(numel, cap, n_d):
+    pl = oracle.plan(numel, cap, n_d)
+    sh_h = _rank_shards_bf16(pl, n_d, 1)
+    sh = [torch.from_numpy(x.view(np.int16)).to(DEV) for x in sh_h]
+    L = z.Layout(numel, cap, n_d, 0)
+    out = torch.full((pl.padded_total,), CANARY, dtype=torch.int16, device=DEV)
+    z.zero_gather_params(L, sh, out)
+    torch.cuda.synchronize()
+    assert_bitwise(u16(out), oracle.gather(sh_h, pl), "gathered flat buffer")
+    if pl.n_buckets >= 3:
+        # a bucket sub-range touches only its own buckets
+        out.fill_(CANARY)
+        z.zero_gather_params(L, sh, out, 1, 2)
+        torch.cuda.synchronize()
+        got = u16(out)
+        exp = oracle.gather(sh_h, pl)
+        lo, hi = pl.padded_off[1], pl.padded_off[1] + pl.padded_len[1]
+        assert_bitwise(got[lo:hi], exp[lo:hi], "bucket 1")
+        assert (got[:lo].view(np.int16) == CANARY).all() and (got[hi:].view(np.int16) == CANARY).all()
+
+
+def test_gather_params_gpt2s_full():
+    w = workloads.get("gpt2s")
+    pl = oracle.plan(w.numel, w.cap, w.n_d)
+    sh_h = _rank_shards_bf16(pl, w.n_d, 2)
+    sh = [torch.from_numpy(x.view(np.int16)).to(DEV) for x in sh_h]
+    out = torch.empty(pl.padded_total, dtype=torch.int16, device=DEV)
+    z.zero_gather_params(z.Layout(w.numel, w.cap, w.n_d, 0), sh, out)
+    torch.cuda.synchronize()
+    assert_bitwise(u16(out), oracle.gather(sh_h, pl), "gpt2s gather")
+
+
+RESHARD = [
+    # numel, (cap, n_d) source, (cap, n_d, rank) destination
+    ([1000, 37, 4096, 3], (1500, 4), (0, 2, 1)),
+    ([5, 0, 123, 64], (40, 3), (16, 5, 4)),
+    ([64 * 300 + 1], (6400, 64), (6400, 8, 7)),
+    ([20000, 20001], (0, 16), (5000, 3, 0)),
+    ([8], (0, 8), (0, 1, 0)),
+]
+
+
+@pytest.mark.parametrize("numel,src,dst", RESHARD)
+def test_reshard_matches_oracle(numel, src, dst):
+    ps = oracle.plan(numel, *src)
+    pd = oracle.plan(numel, dst[0], dst[1])
+    Ls = z.Layout(numel, src[0], src[1], 0)
+    Ld = z.Layout(numel, *dst)
+    for dt, out_type, tdt in ((np.float32, synth.OUT_F32, torch.float32),
+                              (np.uint16, synth.OUT_BF16, torch.int16)):
+        src_h = []
+        for q in range(src[1]):
+            segs = synth.shard_segments(ps.stream_off, ps.len, ps.padded_len, ps.shard_off,
+                                        src[1], q)
+            src_h.append(synth.fill_host(ps.shard_len, out_type, segs,
+                                         synth.key("flat1m", "exp_avg", q), "normal", 1e-4))
+        srcs = [torch.from_numpy(x.view(np.int16) if dt == np.uint16 else x).to(DEV) for x in src_h]
+        out = torch.full((pd.shard_len,), 7, dtype=tdt, device=DEV)
+        z.zero_reshard(Ls, srcs, Ld, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        exp = oracle.reshard(src_h, ps, pd, dst[2])
+        assert_bitwise(got.view(dt) if dt == np.uint16 else got, exp, f"reshard {dt.__name__}")
+
+
+def test_reshard_gpt2s_state_8_to_4_ranks_round_trip():
+    """The optimizer state of GPT-2 small saved from 8 ranks (25 MiB buckets)
+    re-cut for 4 ranks (12.5e6-element buckets) and back: the round trip is
+    the identity and every piece equals the oracle's."""
+    w = workloads.get("gpt2s")
+    ps = oracle.plan(w.numel, w.cap, 8)
+    pd = oracle.plan(w.numel, 12_500_000, 4)
+    Ls = [z.Layout(w.numel, w.cap, 8, r) for r in range(8)]
+    Ld = [z.Layout(w.numel, 12_500_000, 4, r) for r in range(4)]
+    src_h = []
+    for q in range(8):
+        segs = synth.shard_segments(ps.stream_off, ps.len, ps.padded_len, ps.shard_off, 8, q)
+        src_h.append(synth.fill_host(ps.shard_len, synth.OUT_F32, segs,
+                                     synth.key("gpt2s", "master"), "normal", 0.02))
+    srcs = [torch.from_numpy(x).to(DEV) for x in src_h]
+    mid = []
+    for r in range(4):
+        out = torch.empty(pd.shard_len, dtype=torch.float32, device=DEV)
+        z.zero_reshard(Ls[0], srcs, Ld[r], out)
+        mid.append(out)
+    torch.cuda.synchronize()
+    assert_bitwise(mid[3].cpu().numpy(), oracle.reshard(src_h, ps, pd, 3), "8->4 rank 3")
+    for r in range(8):
+        back = torch.empty(ps.shard_len, dtype=torch.float32, device=DEV)
+        z.zero_reshard(Ld[0], mid, Ls[r], back)
+        torch.cuda.synchronize()
+        assert_bitwise(back.cpu().numpy(), src_h[r], f"round trip rank {r}")

@@ -137,6 +137,43 @@ def test_layout_brute_force(seed):
                     assert stream_index(numel, x) == spos[i]
 
 
+@pytest.mark.parametrize("seed", range(25))
+def test_gather_locate_reshard_brute_force(seed):
+    """Gather is the inverse of slicing; locate and reshard agree with the
+    element-by-element planner (labels = stream position + 1, pads = 0)."""
+    rng = np.random.default_rng(500 + seed)
+    numel = [int(v) for v in rng.integers(0, 14, int(rng.integers(1, 6)))]
+    if sum(numel) == 0:
+        numel[0] = 3
+    cap = int(rng.choice([0, 1, 3, 5, 7, 8, 16]))
+    n_d = int(rng.choice([1, 2, 3, 4, 5, 8]))
+    _, _, flat, shards = _brute_layout(numel, cap, n_d)
+    pl = oracle.plan(numel, cap, n_d)
+    lab = lambda x: 0 if x is None else stream_index(numel, x) + 1  # noqa: E731
+    sh = [np.array([lab(x) for x in shards[r]], np.uint16) for r in range(n_d)]
+    assert list(oracle.gather(sh, pl)) == [lab(x) for x in flat]
+    xs = np.arange(sum(numel))
+    r, i = oracle.locate(pl, xs)
+    for x in xs:
+        assert lab(shards[r[x]][i[x]]) == x + 1
+    # reshard to another random layout of the same tensors
+    cap2 = int(rng.choice([0, 2, 4, 6, 9]))
+    n_d2 = int(rng.choice([1, 2, 3, 6]))
+    _, _, _, shards2 = _brute_layout(numel, cap2, n_d2)
+    pl2 = oracle.plan(numel, cap2, n_d2)
+    shf = [a.astype(np.float32) for a in sh]
+    for r2 in range(n_d2):
+        got = oracle.reshard(shf, pl, pl2, r2)
+        assert list(got) == [float(lab(x)) for x in shards2[r2]]
+    back = [oracle.reshard([oracle.reshard(shf, pl, pl2, q) for q in range(n_d2)], pl2, pl, r)
+            for r in range(n_d)]
+    for a, b in zip(back, shf):
+        assert np.array_equal(a, b)
+    same = [oracle.reshard(sh, pl, pl, r) for r in range(n_d)]
+    for a, b in zip(same, sh):
+        assert np.array_equal(a, b)
+
+
 def stream_index(numel, x):
     t, e = x
     return sum(numel[:t]) + e
@@ -257,6 +294,42 @@ def test_reduce_post_divide_equals_pre_divide_pow2():
         for q in range(1, n_d):
             pre = pre + w[q] / np.float32(n_d)
         assert np.array_equal(g.view(np.uint32), pre.view(np.uint32))
+
+
+def test_f32_contributions_equal_bf16_path_on_bf16_values():
+    """fp32 contributions that hold bf16 values give exactly the bf16 path's
+    update (the reduction sees the same binary32 numbers)."""
+    rng = np.random.default_rng(21)
+    n = 5000
+    for n_d in (1, 3, 8, 64):
+        grads = [bf16_of((rng.standard_normal(n) * 1e-3).astype(np.float32)) for _ in range(n_d)]
+        th = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        m0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+        v0 = np.abs(rng.standard_normal(n) * 1e-6).astype(np.float32)
+        a = [th.copy(), m0.copy(), v0.copy()]
+        b = [th.copy(), m0.copy(), v0.copy()]
+        pa, ga = oracle.shard_step(grads, *a, HP, 7, want_grad=True)
+        pb, gb = oracle.shard_step_f32([oracle.widen_bf16(g) for g in grads], *b, HP, 7,
+                                       want_grad=True)
+        assert np.array_equal(pa, pb) and np.array_equal(ga.view(np.uint32), gb.view(np.uint32))
+        for x, y in zip(a, b):
+            assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+def test_f32_reduce_order_and_exact_sums():
+    master, m, v = (np.zeros(1, np.float32) for _ in range(3))
+    vals = [np.array([1.0], np.float32), np.array([2.0 ** -24], np.float32),
+            np.array([-1.0], np.float32)]
+    _, g = oracle.shard_step_f32(vals, master, m, v, HP, 1, want_grad=True)
+    assert g[0] == 0.0
+    rng = np.random.default_rng(22)
+    for n_d in (2, 5, 8):
+        ints = rng.integers(-10 ** 6, 10 ** 6, size=(n_d, 300))
+        G = [ints[q].astype(np.float32) for q in range(n_d)]
+        z3 = [np.zeros(300, np.float32) for _ in range(3)]
+        _, g = oracle.shard_step_f32(G, *z3, HP, 1, want_grad=True)
+        for k in range(300):
+            assert g[k] == np.float32(float(Fraction(int(ints[:, k].sum()), n_d)))
 
 
 # ------------------------------------------------------------------ accumulate
