@@ -23,43 +23,63 @@ namespace {
 using namespace zs;
 
 // ------------------------------------------------------------------ pack
+// A piece is one tensor's part inside one bucket (or a bucket's padding).
+// Work is cut into equal tiles so that ragged tensors (a 38.6M-element
+// embedding next to 768-element norm vectors) keep every block equally busy:
+// block x takes tile x of the launch and finds its piece by binary search
+// over the launch's tile prefix sums.
 struct Piece {
   const uint16_t* src;  // nullptr: write zeros (bucket padding)
   int64_t dst;          // element offset in the flat buffer
   int64_t n;            // element count
+  int64_t head;         // vector pieces: elements before the destination is 16-byte aligned
+  int32_t vec;          // 1: source and destination share 16-byte phase (or zeros)
 };
-constexpr int kPiecesPerLaunch = 64;
+constexpr int kPiecesPerLaunch = 48;
+constexpr int kPackThreads = 256;
+constexpr int64_t kTileVecs = kPackThreads * 4;   // 8-element vectors per tile
+constexpr int64_t kTileElems = kPackThreads * 4;  // elements per tile, scalar pieces
 struct PackArgs {
   Piece p[kPiecesPerLaunch];
+  int64_t tile0[kPiecesPerLaunch + 1];  // first tile of each piece; tile0[n] = total
   uint16_t* out;
+  int32_t n;
 };
 
-__global__ void __launch_bounds__(256) pack_kernel(const PackArgs A) {
-  const Piece pc = A.p[blockIdx.y];
+int64_t piece_tiles(const Piece& pc) {
+  if (!pc.vec) return std::max<int64_t>(1, (pc.n + kTileElems - 1) / kTileElems);
+  const int64_t nv = (pc.n - pc.head) >> 3;
+  return std::max<int64_t>(1, (nv + kTileVecs - 1) / kTileVecs);
+}
+
+__global__ void __launch_bounds__(kPackThreads) pack_kernel(const PackArgs A) {
+  const int64_t tile = blockIdx.x;
+  int lo = 0, hi = A.n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (A.tile0[mid] <= tile) lo = mid;
+    else hi = mid;
+  }
+  const Piece pc = A.p[lo];
+  const int64_t t = tile - A.tile0[lo];
+  const int64_t ntile = A.tile0[lo + 1] - A.tile0[lo];
   uint16_t* d = A.out + pc.dst;
-  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t T = (int64_t)gridDim.x * blockDim.x;
-  const uintptr_t da = (uintptr_t)d;
   const bool zeros = pc.src == nullptr;
-  const bool vec = zeros || (((da ^ (uintptr_t)pc.src) & 15u) == 0);
-  if (!vec) {
-    for (int64_t e = tid; e < pc.n; e += T) d[e] = pc.src[e];
+  if (!pc.vec) {
+    const int64_t e0 = t * kTileElems, e1 = std::min(pc.n, e0 + kTileElems);
+    for (int64_t e = e0 + threadIdx.x; e < e1; e += kPackThreads) d[e] = pc.src[e];
     return;
   }
-  // peel to 16-byte alignment of the destination (same phase as the source)
-  const int64_t head = std::min<int64_t>(pc.n, (int64_t)(((16u - (da & 15u)) & 15u) >> 1));
-  const int64_t nv = (pc.n - head) >> 3;
-  const int64_t tail0 = head + (nv << 3);
-  if (tid < head) d[tid] = zeros ? (uint16_t)0 : pc.src[tid];
-  if (tid < pc.n - tail0) d[tail0 + tid] = zeros ? (uint16_t)0 : pc.src[tail0 + tid];
-  u32x4* dv = (u32x4*)(d + head);
-  if (zeros) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int64_t k = tid; k < nv; k += T) st_stream<false>(dv + k, z);
-  } else {
-    const u32x4* sv = (const u32x4*)(pc.src + head);
-    for (int64_t k = tid; k < nv; k += T) st_stream<false>(dv + k, ld_stream<false>(sv + k));
-  }
+  const int64_t nv = (pc.n - pc.head) >> 3;
+  const int64_t tail0 = pc.head + (nv << 3);
+  if (t == 0 && threadIdx.x < pc.head) d[threadIdx.x] = zeros ? (uint16_t)0 : pc.src[threadIdx.x];
+  if (t == ntile - 1 && threadIdx.x < pc.n - tail0)
+    d[tail0 + threadIdx.x] = zeros ? (uint16_t)0 : pc.src[tail0 + threadIdx.x];
+  u32x4* dv = (u32x4*)(d + pc.head);
+  const u32x4* sv = zeros ? nullptr : (const u32x4*)(pc.src + pc.head);
+  const int64_t v0 = t * kTileVecs, v1 = std::min(nv, v0 + kTileVecs);
+  for (int64_t v = v0 + threadIdx.x; v < v1; v += kPackThreads)
+    st_stream<false>(dv + v, zeros ? u32x4{0u, 0u, 0u, 0u} : ld_stream<false>(sv + v));
 }
 
 // ------------------------------------------------------------------ accumulate
@@ -160,30 +180,34 @@ int zero_bucket_pack(const zero_layout* L, const uint16_t* const* tensor_grads,
       if (a >= z) continue;
       const uint16_t* src = tensor_grads[t];
       if (!src) return ZERO_EINVAL;
-      pieces.push_back(Piece{src + (a - L->tensor_off[t]), base + (a - x0), z - a});
+      pieces.push_back(Piece{src + (a - L->tensor_off[t]), base + (a - x0), z - a, 0, 0});
     }
     const int64_t pad = L->bucket_padded(b) - L->bucket_len(b);
-    if (pad > 0) pieces.push_back(Piece{nullptr, base + L->bucket_len(b), pad});
+    if (pad > 0) pieces.push_back(Piece{nullptr, base + L->bucket_len(b), pad, 0, 0});
+  }
+  // vector eligibility and head peel (destination alignment) per piece
+  for (Piece& pc : pieces) {
+    const uintptr_t da = (uintptr_t)(flat_out + pc.dst);
+    pc.vec = pc.src == nullptr || ((da ^ (uintptr_t)pc.src) & 15u) == 0;
+    pc.head = pc.vec ? std::min<int64_t>(pc.n, (int64_t)(((16u - (da & 15u)) & 15u) >> 1)) : 0;
   }
   // sources must not overlap the destination
   for (int32_t k = 0; k < nt; ++k)
     if (tensor_grads[k] && overlap(tensor_grads[k], 2 * L->numel[k], flat_out, 2 * L->P))
       return ZERO_EOVERLAP;
-  if (pieces.empty()) return ZERO_OK;
-  const int64_t cap = (int64_t)cus() * 8;
   for (size_t p0 = 0; p0 < pieces.size(); p0 += kPiecesPerLaunch) {
     PackArgs A;
     A.out = flat_out;
-    const int cnt = (int)std::min<size_t>(kPiecesPerLaunch, pieces.size() - p0);
-    int64_t maxn = 1;
-    for (int k = 0; k < cnt; ++k) {
+    A.n = (int32_t)std::min<size_t>(kPiecesPerLaunch, pieces.size() - p0);
+    int64_t tiles = 0;
+    for (int k = 0; k < A.n; ++k) {
       A.p[k] = pieces[p0 + k];
-      maxn = std::max(maxn, A.p[k].n);
+      A.tile0[k] = tiles;
+      tiles += piece_tiles(A.p[k]);
     }
-    const int64_t work = (maxn + 7) / 8 + 8;
-    const int gx = (int)std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256,
-                                                               std::max<int64_t>(1, cap / cnt)));
-    hipLaunchKernelGGL(pack_kernel, dim3(gx, cnt), dim3(256), 0, stream, A);
+    A.tile0[A.n] = tiles;
+    if (tiles > 0x7fffffff) return ZERO_ERANGE;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)tiles), dim3(kPackThreads), 0, stream, A);
     if (hipGetLastError() != hipSuccess) return ZERO_EHIP;
   }
   return ZERO_OK;
