@@ -22,6 +22,14 @@ _u16p = C.POINTER(C.c_uint16)
 _f32p = C.POINTER(C.c_float)
 
 
+class _Spec(C.Structure):
+    _fields_ = [("numel", _i64p), ("rows", _i64p), ("n_tensors", C.c_int32), ("cap", C.c_int64),
+                ("n_d", C.c_int32)]
+
+
+_specp = C.POINTER(_Spec)
+
+
 def _load():
     global _lib
     if _lib is not None:
@@ -32,14 +40,16 @@ def _load():
     lib = C.CDLL(_LIB_PATH)
     lib.oracle_round_bf16.argtypes = [_f32p, C.c_int64, _u16p]
     lib.oracle_round_bf16_patterns.argtypes = [C.c_uint64, C.c_uint64, _u16p]
-    lib.oracle_plan_counts.argtypes = [_i64p, C.c_int32, C.c_int64, C.c_int32, _i64p, _i64p, _i64p]
-    lib.oracle_plan_buckets.argtypes = [_i64p, C.c_int32, C.c_int64, C.c_int32] + [_i64p] * 5
-    lib.oracle_plan_tensor_ranges.argtypes = [_i64p, C.c_int32, C.c_int64, C.c_int32, C.c_int32,
-                                              _i64p, _i64p]
-    lib.oracle_plan_map.argtypes = [_i64p, C.c_int32, C.c_int64, C.c_int32, C.c_int32, _i64p,
-                                    C.c_int64, _i64p, _i64p]
-    lib.oracle_pack.argtypes = [C.POINTER(_u16p), _i64p, C.c_int32, C.c_int64, C.c_int32, _u16p]
-    lib.oracle_slice.argtypes = [_u16p, _i64p, C.c_int32, C.c_int64, C.c_int32, C.c_int32, _u16p]
+    lib.oracle_plan_counts.argtypes = [_specp, _i64p, _i64p, _i64p]
+    lib.oracle_plan_buckets.argtypes = [_specp] + [_i64p] * 5
+    lib.oracle_plan_tensor_ranges.argtypes = [_specp, C.c_int32, _i64p, _i64p]
+    lib.oracle_plan_map.argtypes = [_specp, C.c_int32, _i64p, C.c_int64, _i64p, _i64p]
+    lib.oracle_pack.argtypes = [C.POINTER(_u16p), _specp, _u16p]
+    lib.oracle_slice.argtypes = [_u16p, _specp, C.c_int32, _u16p]
+    lib.oracle_gather.argtypes = [C.POINTER(_u16p), _specp, _u16p]
+    lib.oracle_plan_locate.argtypes = [_specp, _i64p, C.c_int64, C.POINTER(C.c_int32), _i64p]
+    lib.oracle_reshard.argtypes = [C.POINTER(C.c_void_p), _specp, _specp, C.c_int32, C.c_void_p,
+                                   C.c_int32]
     lib.oracle_accumulate.argtypes = [_f32p, _u16p, C.c_int64, C.c_float, C.c_int32, C.c_int32,
                                       _u16p]
     lib.oracle_step_scalars.argtypes = [C.c_double] * 5 + [C.c_int64, _f32p]
@@ -47,18 +57,12 @@ def _load():
         C.c_int64, _f32p, _f32p, _f32p, _u16p, _f32p, C.c_int32]
     lib.oracle_shard_step_f32.argtypes = [C.c_int32, C.POINTER(_f32p), C.c_int64] + [
         C.c_double] * 5 + [C.c_int64, _f32p, _f32p, _f32p, _u16p, _f32p, C.c_int32]
-    lib.oracle_shard_step_f32.restype = C.c_int
-    lib.oracle_gather.argtypes = [C.POINTER(_u16p), _i64p, C.c_int32, C.c_int64, C.c_int32, _u16p]
-    lib.oracle_plan_locate.argtypes = [_i64p, C.c_int32, C.c_int64, C.c_int32, _i64p, C.c_int64,
-                                       C.POINTER(C.c_int32), _i64p]
-    lib.oracle_reshard.argtypes = [C.POINTER(C.c_void_p), _i64p, C.c_int32, C.c_int64, C.c_int32,
-                                   C.c_int64, C.c_int32, C.c_int32, C.c_void_p, C.c_int32]
-    for name in ("oracle_gather", "oracle_plan_locate", "oracle_reshard"):
-        getattr(lib, name).restype = C.c_int
     lib.oracle_model_state_bytes.argtypes = [C.c_int32, C.c_int64, C.c_int64, C.c_int32]
     lib.oracle_model_state_bytes.restype = C.c_double
     for name in ("oracle_plan_counts", "oracle_plan_buckets", "oracle_plan_tensor_ranges",
-                 "oracle_plan_map", "oracle_pack", "oracle_slice", "oracle_shard_step"):
+                 "oracle_plan_map", "oracle_pack", "oracle_slice", "oracle_gather",
+                 "oracle_plan_locate", "oracle_reshard", "oracle_shard_step",
+                 "oracle_shard_step_f32"):
         getattr(lib, name).restype = C.c_int
     _lib = lib
     return lib
@@ -111,14 +115,17 @@ class Plan:
     padded_off: np.ndarray
     padded_len: np.ndarray
     shard_off: np.ndarray
+    rows: np.ndarray | None = None
+
+    def spec(self):
+        return _make_spec(self.numel, self.rows, self.cap, self.n_d)
 
     def tensor_ranges(self, rank: int):
         n = self.numel.size
         lo = np.zeros(n, np.int64)
         hi = np.zeros(n, np.int64)
-        _check(_load().oracle_plan_tensor_ranges(_ptr(self.numel, C.c_int64), n, self.cap, self.n_d,
-                                                 rank, _ptr(lo, C.c_int64), _ptr(hi, C.c_int64)),
-               "plan_tensor_ranges")
+        _check(_load().oracle_plan_tensor_ranges(self.spec(), rank, _ptr(lo, C.c_int64),
+                                                 _ptr(hi, C.c_int64)), "plan_tensor_ranges")
         return lo, hi
 
     def map(self, rank: int, idx):
@@ -126,22 +133,30 @@ class Plan:
         idx = _i64(idx)
         flat = np.empty(idx.size, np.int64)
         strm = np.empty(idx.size, np.int64)
-        _check(_load().oracle_plan_map(_ptr(self.numel, C.c_int64), self.numel.size, self.cap,
-                                       self.n_d, rank, _ptr(idx, C.c_int64), idx.size,
+        _check(_load().oracle_plan_map(self.spec(), rank, _ptr(idx, C.c_int64), idx.size,
                                        _ptr(flat, C.c_int64), _ptr(strm, C.c_int64)), "plan_map")
         return flat, strm
 
 
-def plan(numel, cap: int, n_d: int) -> Plan:
+def _make_spec(numel, rows, cap, n_d):
+    sp = _Spec(_ptr(numel, C.c_int64), _ptr(rows, C.c_int64) if rows is not None else None,
+               numel.size, cap, n_d)
+    sp._keep = (numel, rows)  # the arrays must outlive the struct
+    return C.pointer(sp)
+
+
+def plan(numel, cap: int, n_d: int, rows=None) -> Plan:
+    """Bucketed flat layout (rows=None), or FSDP2 per-parameter dim-0 layout
+    when `rows` gives each tensor's dim-0 size (cap is then ignored)."""
     numel = _i64(numel)
+    rows = None if rows is None else _i64(rows)
     lib = _load()
+    sp = _make_spec(numel, rows, cap, n_d)
     nb, pt, sl = C.c_int64(), C.c_int64(), C.c_int64()
-    _check(lib.oracle_plan_counts(_ptr(numel, C.c_int64), numel.size, cap, n_d, C.byref(nb),
-                                  C.byref(pt), C.byref(sl)), "plan_counts")
+    _check(lib.oracle_plan_counts(sp, C.byref(nb), C.byref(pt), C.byref(sl)), "plan_counts")
     arrs = [np.zeros(nb.value, np.int64) for _ in range(5)]
-    _check(lib.oracle_plan_buckets(_ptr(numel, C.c_int64), numel.size, cap, n_d,
-                                   *[_ptr(a, C.c_int64) for a in arrs]), "plan_buckets")
-    return Plan(numel, cap, n_d, nb.value, pt.value, sl.value, *arrs)
+    _check(lib.oracle_plan_buckets(sp, *[_ptr(a, C.c_int64) for a in arrs]), "plan_buckets")
+    return Plan(numel, cap, n_d, nb.value, pt.value, sl.value, *arrs, rows=rows)
 
 
 # ----------------------------------------------------------------- pack / slice
@@ -150,8 +165,7 @@ def pack(tensors, pl: Plan) -> np.ndarray:
     assert len(ts) == pl.numel.size and all(t.size == n for t, n in zip(ts, pl.numel))
     arr = (_u16p * max(1, len(ts)))(*[_ptr(t, C.c_uint16) for t in ts])
     out = np.empty(pl.padded_total, np.uint16)
-    _check(_load().oracle_pack(arr, _ptr(pl.numel, C.c_int64), pl.numel.size, pl.cap, pl.n_d,
-                               _ptr(out, C.c_uint16)), "pack")
+    _check(_load().oracle_pack(arr, pl.spec(), _ptr(out, C.c_uint16)), "pack")
     return out
 
 
@@ -159,8 +173,8 @@ def slice_shard(flat: np.ndarray, pl: Plan, rank: int) -> np.ndarray:
     flat = np.ascontiguousarray(flat, dtype=np.uint16)
     assert flat.size == pl.padded_total
     out = np.empty(pl.shard_len, np.uint16)
-    _check(_load().oracle_slice(_ptr(flat, C.c_uint16), _ptr(pl.numel, C.c_int64), pl.numel.size,
-                                pl.cap, pl.n_d, rank, _ptr(out, C.c_uint16)), "slice")
+    _check(_load().oracle_slice(_ptr(flat, C.c_uint16), pl.spec(), rank, _ptr(out, C.c_uint16)),
+           "slice")
     return out
 
 
@@ -170,8 +184,7 @@ def gather(shards, pl: Plan) -> np.ndarray:
     assert len(ss) == pl.n_d and all(x.size == pl.shard_len for x in ss)
     arr = (_u16p * len(ss))(*[_ptr(x, C.c_uint16) for x in ss])
     out = np.empty(pl.padded_total, np.uint16)
-    _check(_load().oracle_gather(arr, _ptr(pl.numel, C.c_int64), pl.numel.size, pl.cap, pl.n_d,
-                                 _ptr(out, C.c_uint16)), "gather")
+    _check(_load().oracle_gather(arr, pl.spec(), _ptr(out, C.c_uint16)), "gather")
     return out
 
 
@@ -180,9 +193,8 @@ def locate(pl: Plan, xs):
     xs = _i64(xs)
     r = np.empty(xs.size, np.int32)
     i = np.empty(xs.size, np.int64)
-    _check(_load().oracle_plan_locate(_ptr(pl.numel, C.c_int64), pl.numel.size, pl.cap, pl.n_d,
-                                      _ptr(xs, C.c_int64), xs.size, _ptr(r, C.c_int32),
-                                      _ptr(i, C.c_int64)), "plan_locate")
+    _check(_load().oracle_plan_locate(pl.spec(), _ptr(xs, C.c_int64), xs.size,
+                                      _ptr(r, C.c_int32), _ptr(i, C.c_int64)), "plan_locate")
     return r, i
 
 
@@ -194,8 +206,7 @@ def reshard(src_shards, src: Plan, dst: Plan, dst_rank: int) -> np.ndarray:
     assert np.array_equal(src.numel, dst.numel) and len(ss) == src.n_d
     arr = (C.c_void_p * len(ss))(*[x.ctypes.data for x in ss])
     out = np.empty(dst.shard_len, dt)
-    _check(_load().oracle_reshard(arr, _ptr(src.numel, C.c_int64), src.numel.size, src.cap,
-                                  src.n_d, dst.cap, dst.n_d, dst_rank, out.ctypes.data,
+    _check(_load().oracle_reshard(arr, src.spec(), dst.spec(), dst_rank, out.ctypes.data,
                                   dt.itemsize), "reshard")
     return out
 

@@ -94,31 +94,64 @@ struct Plan {
   int64_t padded_total = 0, shard_len = 0;
 };
 
-Plan make_plan(const int64_t* numel, int32_t n_tensors, int64_t cap, int32_t n_d) {
+// What a layout is made from.  rows == nullptr: the bucketed flat layout
+// above (cut every `cap` elements).  rows != nullptr: FSDP2's per-parameter
+// sharding ([DP] "FSDP2": each parameter is split along dim 0; a rank keeps
+// ceil(rows/n_d) rows of every parameter, the last ranks' pieces padded with
+// zero rows): one bucket per tensor, padded to n_d * ceil(rows/n_d) rows.
+struct Spec {
+  const int64_t* numel;
+  const int64_t* rows;
+  int32_t n_tensors;
+  int64_t cap;
+  int32_t n_d;
+};
+
+void add_bucket(Plan& p, int64_t pos, int64_t l, int64_t pl, int32_t n_d) {
+  p.stream_off.push_back(pos);
+  p.len.push_back(l);
+  p.padded_off.push_back(p.padded_total);
+  p.padded_len.push_back(pl);
+  p.shard_off.push_back(p.shard_len);
+  p.padded_total += pl;
+  p.shard_len += pl / n_d;
+}
+
+Plan make_plan(const Spec& sp) {
   Plan p;
-  for (int32_t t = 0; t < n_tensors; ++t) p.total += numel[t];
-  int64_t c = (cap <= 0) ? p.total : cap;
+  const int32_t n_d = sp.n_d;
+  for (int32_t t = 0; t < sp.n_tensors; ++t) p.total += sp.numel[t];
+  if (sp.rows) {
+    int64_t pos = 0;
+    for (int32_t t = 0; t < sp.n_tensors; ++t) {
+      const int64_t r = sp.rows[t], n = sp.numel[t];
+      const int64_t per_row = r > 0 ? n / r : 0;
+      const int64_t c = (r + n_d - 1) / n_d;
+      add_bucket(p, pos, n, (int64_t)n_d * c * per_row, n_d);
+      pos += n;
+    }
+    return p;
+  }
+  int64_t c = (sp.cap <= 0) ? p.total : sp.cap;
   int64_t pos = 0;
   while (pos < p.total) {
     int64_t l = std::min(c, p.total - pos);
-    int64_t pl = ((l + n_d - 1) / n_d) * n_d;
-    p.stream_off.push_back(pos);
-    p.len.push_back(l);
-    p.padded_off.push_back(p.padded_total);
-    p.padded_len.push_back(pl);
-    p.shard_off.push_back(p.shard_len);
-    p.padded_total += pl;
-    p.shard_len += pl / n_d;
+    add_bucket(p, pos, l, ((l + n_d - 1) / n_d) * n_d, n_d);
     pos += l;
   }
   return p;
 }
 
-bool plan_args_ok(const int64_t* numel, int32_t n_tensors, int32_t n_d) {
-  if (n_tensors < 0 || n_d < 1) return false;
-  if (n_tensors > 0 && !numel) return false;
-  for (int32_t t = 0; t < n_tensors; ++t)
-    if (numel[t] < 0) return false;
+bool spec_ok(const Spec* sp) {
+  if (!sp || sp->n_tensors < 0 || sp->n_d < 1) return false;
+  if (sp->n_tensors > 0 && !sp->numel) return false;
+  for (int32_t t = 0; t < sp->n_tensors; ++t) {
+    if (sp->numel[t] < 0) return false;
+    if (sp->rows) {
+      const int64_t r = sp->rows[t];
+      if (r < 0 || (r == 0 && sp->numel[t] != 0) || (r > 0 && sp->numel[t] % r != 0)) return false;
+    }
+  }
   return true;
 }
 
@@ -231,10 +264,10 @@ void oracle_round_bf16_patterns(uint64_t lo, uint64_t hi, uint16_t* out) {
 // Pinned by: the FSDP1 worked example (golden fixture), brute force against an
 // element-by-element planner on tiny inputs, and closed-form invariants.
 // Returns 0, or -1 on bad arguments.
-int oracle_plan_counts(const int64_t* numel, int32_t n_tensors, int64_t cap, int32_t n_d,
-                       int64_t* n_buckets, int64_t* padded_total, int64_t* shard_len) {
-  if (!plan_args_ok(numel, n_tensors, n_d)) return -1;
-  Plan p = make_plan(numel, n_tensors, cap, n_d);
+int oracle_plan_counts(const Spec* sp, int64_t* n_buckets, int64_t* padded_total,
+                       int64_t* shard_len) {
+  if (!spec_ok(sp)) return -1;
+  Plan p = make_plan(*sp);
   *n_buckets = (int64_t)p.len.size();
   *padded_total = p.padded_total;
   *shard_len = p.shard_len;
@@ -242,11 +275,10 @@ int oracle_plan_counts(const int64_t* numel, int32_t n_tensors, int64_t cap, int
 }
 
 // Per-bucket arrays, each of n_buckets entries.
-int oracle_plan_buckets(const int64_t* numel, int32_t n_tensors, int64_t cap, int32_t n_d,
-                        int64_t* stream_off, int64_t* len, int64_t* padded_off,
+int oracle_plan_buckets(const Spec* sp, int64_t* stream_off, int64_t* len, int64_t* padded_off,
                         int64_t* padded_len, int64_t* shard_off) {
-  if (!plan_args_ok(numel, n_tensors, n_d)) return -1;
-  Plan p = make_plan(numel, n_tensors, cap, n_d);
+  if (!spec_ok(sp)) return -1;
+  Plan p = make_plan(*sp);
   for (size_t b = 0; b < p.len.size(); ++b) {
     stream_off[b] = p.stream_off[b];
     len[b] = p.len[b];
@@ -262,13 +294,13 @@ int oracle_plan_buckets(const int64_t* numel, int32_t n_tensors, int64_t cap, in
 // The shard lists owned stream positions in stream order and a tensor is a
 // stream interval, so nothing of another tensor falls inside the range; bucket
 // padding can (when a tensor continues past a padded bucket end).
-int oracle_plan_tensor_ranges(const int64_t* numel, int32_t n_tensors, int64_t cap, int32_t n_d,
-                              int32_t rank, int64_t* lo, int64_t* hi) {
-  if (!plan_args_ok(numel, n_tensors, n_d) || rank < 0 || rank >= n_d) return -1;
-  Plan p = make_plan(numel, n_tensors, cap, n_d);
+int oracle_plan_tensor_ranges(const Spec* sp, int32_t rank, int64_t* lo, int64_t* hi) {
+  if (!spec_ok(sp) || rank < 0 || rank >= sp->n_d) return -1;
+  const int32_t n_d = sp->n_d;
+  Plan p = make_plan(*sp);
   int64_t a = 0;
-  for (int32_t t = 0; t < n_tensors; ++t) {
-    int64_t z = a + numel[t];
+  for (int32_t t = 0; t < sp->n_tensors; ++t) {
+    int64_t z = a + sp->numel[t];
     int64_t first = -1, last = -1;
     for (size_t b = 0; b < p.len.size(); ++b) {
       int64_t sb = p.padded_len[b] / n_d;
@@ -289,10 +321,11 @@ int oracle_plan_tensor_ranges(const int64_t* numel, int32_t n_tensors, int64_t c
 
 // For rank r and n shard indices: the position in the padded flat buffer
 // (`flat_pos`) and in the unpadded stream (`stream_pos`, -1 for a pad).
-int oracle_plan_map(const int64_t* numel, int32_t n_tensors, int64_t cap, int32_t n_d, int32_t rank,
-                    const int64_t* idx, int64_t n, int64_t* flat_pos, int64_t* stream_pos) {
-  if (!plan_args_ok(numel, n_tensors, n_d) || rank < 0 || rank >= n_d) return -1;
-  Plan p = make_plan(numel, n_tensors, cap, n_d);
+int oracle_plan_map(const Spec* sp, int32_t rank, const int64_t* idx, int64_t n,
+                    int64_t* flat_pos, int64_t* stream_pos) {
+  if (!spec_ok(sp) || rank < 0 || rank >= sp->n_d) return -1;
+  const int32_t n_d = sp->n_d;
+  Plan p = make_plan(*sp);
   for (int64_t k = 0; k < n; ++k) {
     if (idx[k] < 0 || idx[k] >= p.shard_len) return -1;
     int64_t b = bucket_of_shard_index(p, idx[k]);
@@ -309,14 +342,13 @@ int oracle_plan_map(const int64_t* numel, int32_t n_tensors, int64_t cap, int32_
 // one after another in the flat buffer; padding is zero.
 // Pinned by: brute force against a plain concatenation on tiny inputs and the
 // FSDP1 example.
-int oracle_pack(const uint16_t* const* tensors, const int64_t* numel, int32_t n_tensors, int64_t cap,
-                int32_t n_d, uint16_t* flat_out) {
-  if (!plan_args_ok(numel, n_tensors, n_d)) return -1;
-  Plan p = make_plan(numel, n_tensors, cap, n_d);
+int oracle_pack(const uint16_t* const* tensors, const Spec* sp, uint16_t* flat_out) {
+  if (!spec_ok(sp)) return -1;
+  Plan p = make_plan(*sp);
   for (int64_t k = 0; k < p.padded_total; ++k) flat_out[k] = 0;
   int64_t x = 0, b = 0;  // stream position and the bucket holding it
-  for (int32_t t = 0; t < n_tensors; ++t) {
-    for (int64_t e = 0; e < numel[t]; ++e, ++x) {
+  for (int32_t t = 0; t < sp->n_tensors; ++t) {
+    for (int64_t e = 0; e < sp->numel[t]; ++e, ++x) {
       while (b + 1 < (int64_t)p.len.size() && p.stream_off[b + 1] <= x) ++b;
       flat_out[p.padded_off[b] + (x - p.stream_off[b])] = tensors[t][e];
     }
@@ -326,10 +358,10 @@ int oracle_pack(const uint16_t* const* tensors, const int64_t* numel, int32_t n_
 
 // Gather rank r's shard (its slice of every bucket, in bucket order) out of a
 // padded flat buffer.
-int oracle_slice(const uint16_t* flat, const int64_t* numel, int32_t n_tensors, int64_t cap,
-                 int32_t n_d, int32_t rank, uint16_t* shard_out) {
-  if (!plan_args_ok(numel, n_tensors, n_d) || rank < 0 || rank >= n_d) return -1;
-  Plan p = make_plan(numel, n_tensors, cap, n_d);
+int oracle_slice(const uint16_t* flat, const Spec* sp, int32_t rank, uint16_t* shard_out) {
+  if (!spec_ok(sp) || rank < 0 || rank >= sp->n_d) return -1;
+  const int32_t n_d = sp->n_d;
+  Plan p = make_plan(*sp);
   for (size_t b = 0; b < p.len.size(); ++b) {
     int64_t sb = p.padded_len[b] / n_d;
     for (int64_t j = 0; j < sb; ++j)
@@ -345,10 +377,10 @@ int oracle_slice(const uint16_t* flat, const int64_t* numel, int32_t n_tensors, 
 // goes back to slot q of that bucket.
 // Pinned by: gather(slices of x) == x for packed x (inverse of the pinned
 // slice), brute force on tiny layouts.
-int oracle_gather(const uint16_t* const* shards, const int64_t* numel, int32_t n_tensors,
-                  int64_t cap, int32_t n_d, uint16_t* out) {
-  if (!plan_args_ok(numel, n_tensors, n_d)) return -1;
-  Plan p = make_plan(numel, n_tensors, cap, n_d);
+int oracle_gather(const uint16_t* const* shards, const Spec* sp, uint16_t* out) {
+  if (!spec_ok(sp)) return -1;
+  const int32_t n_d = sp->n_d;
+  Plan p = make_plan(*sp);
   for (size_t b = 0; b < p.len.size(); ++b) {
     int64_t sb = p.padded_len[b] / n_d;
     for (int32_t q = 0; q < n_d; ++q)
@@ -359,10 +391,11 @@ int oracle_gather(const uint16_t* const* shards, const int64_t* numel, int32_t n
 }
 
 // Stream positions -> (owning rank, index in that rank's shard).
-int oracle_plan_locate(const int64_t* numel, int32_t n_tensors, int64_t cap, int32_t n_d,
-                       const int64_t* xs, int64_t n, int32_t* rank, int64_t* idx) {
-  if (!plan_args_ok(numel, n_tensors, n_d)) return -1;
-  Plan p = make_plan(numel, n_tensors, cap, n_d);
+int oracle_plan_locate(const Spec* sp, const int64_t* xs, int64_t n, int32_t* rank,
+                       int64_t* idx) {
+  if (!spec_ok(sp)) return -1;
+  const int32_t n_d = sp->n_d;
+  Plan p = make_plan(*sp);
   for (int64_t k = 0; k < n; ++k) {
     if (xs[k] < 0 || xs[k] >= p.total) return -1;
     auto it = std::upper_bound(p.stream_off.begin(), p.stream_off.end(), xs[k]);
@@ -383,13 +416,16 @@ int oracle_plan_locate(const int64_t* numel, int32_t n_tensors, int64_t cap, int
 // shards, 0 at destination padding.  elem_bytes is 2 or 4.
 // Pinned by: identity on the same layout, A->B->A round trip, labelled
 // elements landing at the brute-force planner's positions.
-int oracle_reshard(const void* const* src, const int64_t* numel, int32_t n_tensors,
-                   int64_t src_cap, int32_t src_nd, int64_t dst_cap, int32_t dst_nd,
+int oracle_reshard(const void* const* src, const Spec* src_sp, const Spec* dst_sp,
                    int32_t dst_rank, void* dst, int32_t elem_bytes) {
-  if (!plan_args_ok(numel, n_tensors, src_nd) || !plan_args_ok(numel, n_tensors, dst_nd)) return -1;
+  if (!spec_ok(src_sp) || !spec_ok(dst_sp)) return -1;
+  if (src_sp->n_tensors != dst_sp->n_tensors) return -1;
+  for (int32_t t = 0; t < src_sp->n_tensors; ++t)
+    if (src_sp->numel[t] != dst_sp->numel[t]) return -1;
+  const int32_t src_nd = src_sp->n_d, dst_nd = dst_sp->n_d;
   if (dst_rank < 0 || dst_rank >= dst_nd || (elem_bytes != 2 && elem_bytes != 4)) return -1;
-  Plan ps = make_plan(numel, n_tensors, src_cap, src_nd);
-  Plan pd = make_plan(numel, n_tensors, dst_cap, dst_nd);
+  Plan ps = make_plan(*src_sp);
+  Plan pd = make_plan(*dst_sp);
   for (int64_t i = 0; i < pd.shard_len; ++i) {
     int64_t b = bucket_of_shard_index(pd, i);
     int64_t sb = pd.padded_len[b] / dst_nd;

@@ -203,6 +203,87 @@ def test_layout_fsdp1_worked_example():
                 assert lo[t] == hi[t]  # the rank holds none of this tensor: empty view
 
 
+def _brute_dim0(shapes, n_d):
+    """FSDP2 per-parameter layout, element by element: tensor t of shape
+    (rows, ...) gives rank r rows [r*c, (r+1)*c), c = ceil(rows/n_d), with
+    missing rows as padding; a rank's shard is its pieces in tensor order;
+    the gathered buffer holds each tensor padded to n_d*c rows."""
+    flat, shards = [], [[] for _ in range(n_d)]
+    for t, shp in enumerate(shapes):
+        rows = shp[0]
+        per_row = int(np.prod(shp[1:])) if len(shp) > 1 else 1
+        c = -(-rows // n_d)
+        for r in range(n_d):
+            for row in range(r * c, (r + 1) * c):
+                for k in range(per_row):
+                    x = (t, row * per_row + k) if row < rows else None
+                    shards[r].append(x)
+                    flat.append(x)
+    return flat, shards
+
+
+def test_fsdp2_worked_examples():
+    """The FSDP2 figure and text: three (4, 2) weights over 2 ranks give each
+    rank the first / last two rows of every weight, local shape (2, 2), 12
+    elements per rank; an (8, 4) weight over 4 ranks has local shape (2, 4)."""
+    g = json.load(open(os.path.join(GOLDEN, "fsdp2_shard0.json")))
+    for case in g["cases"]:
+        shapes = [tuple(x) for x in case["shapes"]]
+        n_d = case["n_d"]
+        numel = [int(np.prod(x)) for x in shapes]
+        pl = oracle.plan(numel, 0, n_d, rows=[x[0] for x in shapes])
+        assert pl.shard_len == case["elems_per_rank"]
+        for t, (shp, loc) in enumerate(zip(shapes, case["local_shapes"])):
+            assert pl.padded_len[t] // n_d == int(np.prod(loc))
+        tensors = [np.arange(1, n + 1, dtype=np.uint16) + 100 * t for t, n in enumerate(numel)]
+        flat = oracle.pack(tensors, pl)
+        for r in range(n_d):
+            shard = oracle.slice_shard(flat, pl, r)
+            rr = case.get("rank_rows", {}).get(str(r))
+            if rr:
+                expect = np.concatenate([tensors[t].reshape(shapes[t])[a:b].ravel()
+                                         for t, (a, b) in enumerate(rr)])
+                assert np.array_equal(shard, expect)
+            lo, hi = pl.tensor_ranges(r)
+            for t, shp in enumerate(shapes):
+                assert hi[t] - lo[t] == int(np.prod(case["local_shapes"][t]))
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_fsdp2_layout_brute_force(seed):
+    rng = np.random.default_rng(700 + seed)
+    n_t = int(rng.integers(1, 5))
+    shapes = [tuple(int(v) for v in rng.integers(1, 7, int(rng.integers(1, 3)))) for _ in range(n_t)]
+    if rng.random() < 0.3:
+        shapes.append((0, 3))
+    n_d = int(rng.choice([1, 2, 3, 4, 5, 8]))
+    numel = [int(np.prod(x)) for x in shapes]
+    flat, shards = _brute_dim0(shapes, n_d)
+    pl = oracle.plan(numel, 0, n_d, rows=[x[0] for x in shapes])
+    assert pl.padded_total == len(flat) == n_d * pl.shard_len
+    lab = {(t, e): 1 + 16 * t + e for t, n in enumerate(numel) for e in range(n)}
+    tensors = [np.array([lab[(t, e)] for e in range(n)], np.uint16) for t, n in enumerate(numel)]
+    packed = oracle.pack(tensors, pl)
+    assert list(packed) == [0 if x is None else lab[x] for x in flat]
+    for r in range(n_d):
+        assert list(oracle.slice_shard(packed, pl, r)) == [0 if x is None else lab[x]
+                                                          for x in shards[r]]
+        if pl.shard_len:
+            fpos, spos = pl.map(r, np.arange(pl.shard_len))
+            for i, x in enumerate(shards[r]):
+                assert flat[fpos[i]] == x
+                assert spos[i] == (-1 if x is None else stream_index(numel, x))
+    sh = [oracle.slice_shard(packed, pl, r) for r in range(n_d)]
+    assert np.array_equal(oracle.gather(sh, pl), packed)
+    # re-cut between the dim-0 layout and a bucketed one, both ways
+    pb = oracle.plan(numel, 5, 3)
+    shf = [a.astype(np.float32) for a in sh]
+    there = [oracle.reshard(shf, pl, pb, q) for q in range(3)]
+    back = [oracle.reshard(there, pb, pl, r) for r in range(n_d)]
+    for a, b in zip(back, shf):
+        assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("name", workloads.NAMES)
 def test_layout_workload_sizes_closed_form(name):
     """Fixed-cut buckets: nb = ceil(psi/C), S = (nb-1)*ceil(C/n_d) + ceil(last/n_d)."""
