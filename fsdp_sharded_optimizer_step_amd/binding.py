@@ -25,7 +25,7 @@ EXPORTS = ("zero_layout_create", "zero_layout_destroy", "zero_layout_psi", "zero
            "zero_layout_shard", "zero_layout_n_buckets", "zero_layout_n_d", "zero_layout_rank",
            "zero_layout_bucket", "zero_layout_tensor", "zero_bucket_pack", "zero_grad_accumulate",
            "zero_shard_step", "zero_shard_step_ex", "zero_step_scalars", "zero_strerror",
-           "zero_gather_params", "zero_reshard")
+           "zero_gather_params", "zero_reshard", "zero_layout_create_dim0", "zero_layout_kind")
 
 
 class ZeroError(RuntimeError):
@@ -63,6 +63,10 @@ def load():
     vp = C.c_void_p
     lib.zero_layout_create.argtypes = [_i64p, C.c_int32, C.c_int64, C.c_int32, C.c_int32,
                                        C.POINTER(vp)]
+    lib.zero_layout_create_dim0.argtypes = [_i64p, _i64p, C.c_int32, C.c_int32, C.c_int32,
+                                            C.POINTER(vp)]
+    lib.zero_layout_kind.argtypes = [vp]
+    lib.zero_layout_kind.restype = C.c_int32
     lib.zero_layout_destroy.argtypes = [vp]
     lib.zero_layout_destroy.restype = None
     for name in ("zero_layout_psi", "zero_layout_padded", "zero_layout_shard",
@@ -117,12 +121,19 @@ class AdamW:
 class Layout:
     """Owning wrapper of a zero_layout (host object)."""
 
-    def __init__(self, numel, bucket_cap: int, n_d: int, rank: int):
+    def __init__(self, numel, bucket_cap: int, n_d: int, rank: int, rows=None):
+        """Bucketed flat layout; with `rows` (each tensor's dim-0 size) the
+        per-parameter dim-0 layout instead (bucket_cap is then unused)."""
         lib = load()
         arr = (C.c_int64 * max(1, len(numel)))(*[int(n) for n in numel])
         h = C.c_void_p()
-        _check("zero_layout_create", lib.zero_layout_create(arr, len(numel), int(bucket_cap),
-                                                            int(n_d), int(rank), C.byref(h)))
+        if rows is None:
+            _check("zero_layout_create", lib.zero_layout_create(
+                arr, len(numel), int(bucket_cap), int(n_d), int(rank), C.byref(h)))
+        else:
+            rarr = (C.c_int64 * max(1, len(rows)))(*[int(r) for r in rows])
+            _check("zero_layout_create_dim0", lib.zero_layout_create_dim0(
+                arr, rarr, len(numel), int(n_d), int(rank), C.byref(h)))
         self._h = h
         self.n_tensors = len(numel)
 
@@ -142,6 +153,7 @@ class Layout:
     n_buckets = property(lambda self: load().zero_layout_n_buckets(self._h))
     n_d = property(lambda self: load().zero_layout_n_d(self._h))
     rank = property(lambda self: load().zero_layout_rank(self._h))
+    kind = property(lambda self: load().zero_layout_kind(self._h))
 
     def bucket(self, b: int):
         """-> (stream_off, len, padded_off, padded_len, shard_off)"""

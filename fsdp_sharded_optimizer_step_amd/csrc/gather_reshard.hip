@@ -38,6 +38,13 @@ Geo geo_of(const zero_layout& L) {
   return Geo{L.cap, L.nb, L.s_full, L.p_full, L.len_last, L.s_last, L.n_d, L.rank};
 }
 
+// Bucket b of any layout seen as a one-bucket layout of its own (addresses
+// relative to the bucket's stream, padded and shard offsets).
+Geo geo_of_bucket(const zero_layout& L, int64_t b) {
+  const int64_t sl = L.bucket_slice(b), len = L.bucket_len(b);
+  return Geo{len > 0 ? len : 1, 1, sl, sl * L.n_d, len, sl, L.n_d, L.rank};
+}
+
 __device__ __forceinline__ int64_t slice_len(const Geo& g, int64_t b) {
   return b + 1 < g.nb ? g.s_full : g.s_last;
 }
@@ -92,11 +99,20 @@ __global__ void __launch_bounds__(256) gather_scalar_kernel(const GatherArgs A) 
 }
 
 // ------------------------------------------------------------------ reshard
+// One launch covers the destination shard indices [i0, i0 + n).  The
+// destination index i maps to the stream position
+//   x = d_base_x + stream_of(gd, i - d_base_i)     (or padding)
+// and, when has_src, the source element is found by
+//   locate(gs, x - s_base_x)   if 0 <= x - s_base_x < s_len
+// in the source shards (pointers already shifted to the source bucket).
+// Padding is written as zero when zero_pads; positions whose stream element
+// lies outside this launch's source range are left alone.
 struct ReshardArgs {
   const void* src[ZERO_MAX_ND];
   void* dst;
   Geo gs, gd;
-  int64_t n;  // destination shard length
+  int64_t i0, n, d_base_i, d_base_x, s_base_x, s_len;
+  int32_t zero_pads, has_src;
 };
 
 // Destination shard index -> stream position (or -1 for padding).
@@ -121,16 +137,20 @@ __device__ __forceinline__ void locate(const Geo& g, int64_t x, int32_t& q, int6
 template <class T>
 __global__ void __launch_bounds__(256) reshard_kernel(const ReshardArgs A) {
   const int64_t T_ = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < A.n; i += T_) {
-    const int64_t x = stream_of(A.gd, i);
-    T val = T(0);
-    if (x >= 0) {
-      int32_t q;
-      int64_t idx;
-      locate(A.gs, x, q, idx);
-      val = ((const T*)A.src[q])[idx];
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < A.n; e += T_) {
+    const int64_t i = A.i0 + e;
+    const int64_t xl = stream_of(A.gd, i - A.d_base_i);
+    if (xl < 0) {
+      if (A.zero_pads) ((T*)A.dst)[i] = T(0);
+      continue;
     }
-    ((T*)A.dst)[i] = val;
+    if (!A.has_src) continue;
+    const int64_t xs = A.d_base_x + xl - A.s_base_x;
+    if (xs < 0 || xs >= A.s_len) continue;
+    int32_t q;
+    int64_t idx;
+    locate(A.gs, xs, q, idx);
+    ((T*)A.dst)[i] = ((const T*)A.src[q])[idx];
   }
 }
 
@@ -169,21 +189,37 @@ int zero_gather_params(const zero_layout* L, const uint16_t* const* rank_shards,
     if (overlap(rank_shards[q], 2 * L->S, full_out, 2 * L->P)) return ZERO_EOVERLAP;
   }
   if (bucket_begin == bucket_end) return ZERO_OK;
-  GatherArgs A;
-  for (int q = 0; q < ZERO_MAX_ND; ++q) A.shard[q] = q < nd ? rank_shards[q] : nullptr;
-  A.out = full_out;
-  A.g = geo_of(*L);
-  A.f0 = L->bucket_padded_off(bucket_begin);
-  A.f1 = L->bucket_padded_off(bucket_end - 1) + L->bucket_padded(bucket_end - 1);
-  bool vec = a16(full_out) && L->s_full % 8 == 0 && L->s_last % 8 == 0;
-  for (int32_t q = 0; q < nd; ++q) vec = vec && a16(rank_shards[q]);
-  if (vec)
-    hipLaunchKernelGGL(gather_vec_kernel, dim3(blocks_for((A.f1 - A.f0) >> 3)), dim3(256), 0,
-                       stream, A);
-  else
-    hipLaunchKernelGGL(gather_scalar_kernel, dim3(blocks_for(A.f1 - A.f0)), dim3(256), 0, stream,
-                       A);
-  return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
+  auto launch = [&](const Geo& g, int64_t shard_shift, int64_t out_shift, int64_t f0,
+                    int64_t f1) -> int {
+    GatherArgs A;
+    for (int q = 0; q < ZERO_MAX_ND; ++q)
+      A.shard[q] = q < nd ? rank_shards[q] + shard_shift : nullptr;
+    A.out = full_out + out_shift;
+    A.g = g;
+    A.f0 = f0;
+    A.f1 = f1;
+    bool vec = a16(A.out) && g.s_full % 8 == 0 && g.s_last % 8 == 0 && f0 % 8 == 0;
+    for (int32_t q = 0; q < nd; ++q) vec = vec && a16(A.shard[q]);
+    if (vec)
+      hipLaunchKernelGGL(gather_vec_kernel, dim3(blocks_for((f1 - f0) >> 3)), dim3(256), 0,
+                         stream, A);
+    else
+      hipLaunchKernelGGL(gather_scalar_kernel, dim3(blocks_for(f1 - f0)), dim3(256), 0, stream,
+                         A);
+    return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
+  };
+  if (L->fixed()) {
+    const int64_t f0 = L->bucket_padded_off(bucket_begin);
+    const int64_t f1 = L->bucket_padded_off(bucket_end - 1) + L->bucket_padded(bucket_end - 1);
+    return launch(geo_of(*L), 0, 0, f0, f1);
+  }
+  for (int64_t b = bucket_begin; b < bucket_end; ++b) {
+    if (L->bucket_slice(b) == 0) continue;
+    const int rc = launch(geo_of_bucket(*L, b), L->bucket_shard_off(b), L->bucket_padded_off(b),
+                          0, L->bucket_padded(b));
+    if (rc != ZERO_OK) return rc;
+  }
+  return ZERO_OK;
 }
 
 int zero_reshard(const zero_layout* src, const void* const* src_shards, const zero_layout* dst,
@@ -197,17 +233,68 @@ int zero_reshard(const zero_layout* src, const void* const* src_shards, const ze
       return ZERO_EOVERLAP;
   }
   if (dst->S == 0) return ZERO_OK;
-  ReshardArgs A;
-  for (int q = 0; q < ZERO_MAX_ND; ++q) A.src[q] = q < src->n_d ? src_shards[q] : nullptr;
-  A.dst = dst_shard;
-  A.gs = geo_of(*src);
-  A.gd = geo_of(*dst);
-  A.n = dst->S;
-  if (elem_bytes == 4)
-    hipLaunchKernelGGL(reshard_kernel<uint32_t>, dim3(blocks_for(A.n)), dim3(256), 0, stream, A);
-  else
-    hipLaunchKernelGGL(reshard_kernel<uint16_t>, dim3(blocks_for(A.n)), dim3(256), 0, stream, A);
-  return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
+
+  // One launch: destination range [i0, i0+n) read through geometry gd
+  // (origin d_base_i / d_base_x), source through gs with its pointers
+  // shifted by s_shift elements and stream origin s_base_x.
+  auto launch = [&](const Geo& gd, int64_t i0, int64_t n, int64_t d_base_i, int64_t d_base_x,
+                    const Geo* gs, int64_t s_shift, int64_t s_base_x, int64_t s_len,
+                    bool zero_pads) -> int {
+    if (n <= 0) return ZERO_OK;
+    ReshardArgs A;
+    for (int q = 0; q < ZERO_MAX_ND; ++q)
+      A.src[q] = q < src->n_d ? (const char*)src_shards[q] + s_shift * elem_bytes : nullptr;
+    A.dst = dst_shard;
+    A.gd = gd;
+    A.gs = gs ? *gs : gd;
+    A.i0 = i0;
+    A.n = n;
+    A.d_base_i = d_base_i;
+    A.d_base_x = d_base_x;
+    A.s_base_x = s_base_x;
+    A.s_len = s_len;
+    A.zero_pads = zero_pads ? 1 : 0;
+    A.has_src = gs ? 1 : 0;
+    if (elem_bytes == 4)
+      hipLaunchKernelGGL(reshard_kernel<uint32_t>, dim3(blocks_for(n)), dim3(256), 0, stream, A);
+    else
+      hipLaunchKernelGGL(reshard_kernel<uint16_t>, dim3(blocks_for(n)), dim3(256), 0, stream, A);
+    return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
+  };
+
+  int rc = ZERO_OK;
+  if (src->fixed()) {
+    const Geo gs = geo_of(*src);
+    if (dst->fixed())
+      return launch(geo_of(*dst), 0, dst->S, 0, 0, &gs, 0, 0, src->psi, true);
+    for (int64_t b = 0; b < dst->nb && rc == ZERO_OK; ++b)
+      rc = launch(geo_of_bucket(*dst, b), dst->bucket_shard_off(b), dst->bucket_slice(b),
+                  dst->bucket_shard_off(b), dst->bucket_stream_off(b), &gs, 0, 0, src->psi, true);
+    return rc;
+  }
+  // per-parameter source: one launch per source tensor over the destination
+  // indices that can hold it; destination padding first when the
+  // destination is bucketed
+  if (dst->fixed()) {
+    const Geo gd = geo_of(*dst);
+    rc = launch(gd, 0, dst->S, 0, 0, nullptr, 0, 0, 0, true);
+    for (int64_t t = 0; t < src->nb && rc == ZERO_OK; ++t) {
+      if (src->bucket_len(t) == 0) continue;
+      int64_t lo = 0, hi = 0;
+      zero_layout_tensor(dst, (int32_t)t, nullptr, &lo, &hi);
+      const Geo gs = geo_of_bucket(*src, t);
+      rc = launch(gd, lo, hi - lo, 0, 0, &gs, src->bucket_shard_off(t), src->bucket_stream_off(t),
+                  src->bucket_len(t), false);
+    }
+    return rc;
+  }
+  for (int64_t t = 0; t < src->nb && rc == ZERO_OK; ++t) {
+    const Geo gs = geo_of_bucket(*src, t);
+    rc = launch(geo_of_bucket(*dst, t), dst->bucket_shard_off(t), dst->bucket_slice(t),
+                dst->bucket_shard_off(t), dst->bucket_stream_off(t), &gs,
+                src->bucket_shard_off(t), src->bucket_stream_off(t), src->bucket_len(t), true);
+  }
+  return rc;
 }
 
 }  // extern "C"

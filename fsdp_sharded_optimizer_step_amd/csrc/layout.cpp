@@ -59,6 +59,53 @@ int zero_layout_create(const int64_t* numel, int32_t n_tensors, int64_t bucket_c
   return ZERO_OK;
 }
 
+int zero_layout_create_dim0(const int64_t* numel, const int64_t* rows, int32_t n_tensors,
+                            int32_t n_d, int32_t rank, zero_layout** out) {
+  if (!out || n_tensors < 0 || (n_tensors > 0 && (!numel || !rows))) return ZERO_EINVAL;
+  if (n_d < 1 || n_d > ZERO_MAX_ND) return ZERO_EINVAL;
+  if (rank < 0 || rank >= n_d) return ZERO_ERANGE;
+  int64_t psi = 0;
+  for (int32_t t = 0; t < n_tensors; ++t) {
+    const int64_t r = rows[t], n = numel[t];
+    if (n < 0 || r < 0 || (r == 0 && n != 0) || (r > 0 && n % r != 0)) return ZERO_EINVAL;
+    if (n > std::numeric_limits<int64_t>::max() / 4 - psi) return ZERO_ERANGE;
+    psi += n;
+  }
+  zero_layout* L = new (std::nothrow) zero_layout;
+  if (!L) return ZERO_EINVAL;
+  L->kind = zero_layout::DIM0;
+  L->n_d = n_d;
+  L->rank = rank;
+  L->psi = psi;
+  L->numel.assign(numel, numel + n_tensors);
+  L->nb = n_tensors;
+  L->tensor_off.resize(n_tensors);
+  L->t_len.resize(n_tensors);
+  L->t_slice.resize(n_tensors);
+  L->t_padded_off.resize(n_tensors);
+  L->t_shard_off.resize(n_tensors);
+  int64_t off = 0, poff = 0, soff = 0;
+  for (int32_t t = 0; t < n_tensors; ++t) {
+    const int64_t r = rows[t], n = numel[t];
+    const int64_t per_row = r > 0 ? n / r : 0;
+    const int64_t slice = ceil_div(r, n_d) * per_row;
+    L->tensor_off[t] = off;
+    L->t_len[t] = n;
+    L->t_slice[t] = slice;
+    L->t_padded_off[t] = poff;
+    L->t_shard_off[t] = soff;
+    off += n;
+    poff += slice * n_d;
+    soff += slice;
+  }
+  L->P = poff;
+  L->S = soff;
+  *out = L;
+  return ZERO_OK;
+}
+
+int32_t zero_layout_kind(const zero_layout* L) { return L ? L->kind : -1; }
+
 void zero_layout_destroy(zero_layout* layout) { delete layout; }
 
 int64_t zero_layout_psi(const zero_layout* L) { return L ? L->psi : -1; }
@@ -88,7 +135,8 @@ int zero_layout_tensor(const zero_layout* L, int32_t t, int64_t* stream_off, int
   if (stream_off) *stream_off = a;
   int64_t lo = 0, hi = 0;
   if (z > a) {
-    const int64_t b_first = a / L->cap, b_last = (z - 1) / L->cap;
+    const int64_t b_first = L->fixed() ? a / L->cap : t;
+    const int64_t b_last = L->fixed() ? (z - 1) / L->cap : t;
     bool found = false;
     for (int64_t b = b_first; b <= b_last && !found; ++b) {
       int64_t olo, ohi;

@@ -22,6 +22,7 @@
 // bytes are in flight.
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "device_common.hpp"
 #include "layout.hpp"
@@ -479,38 +480,47 @@ int zero_shard_step_ex(const zero_layout* L, const zero_adamw* hp, int64_t t,
   // With it: part 0 = the full buckets, part 1 = the last bucket; one vector
   // launch covers both when every vector address is aligned, otherwise the
   // parts that are not aligned go to the scalar kernel.
-  Region regs[2];
-  bool vec[2] = {false, false};
-  int nreg = 0;
+  std::vector<Region> regs;
+  std::vector<bool> vec;
   const int64_t r = L->rank;
-  if (!map) {
-    regs[nreg] = Region{0, S, S, S, 0, 0, 0};
-    vec[nreg++] = allow_vec;
+  if (map && !L->fixed()) {
+    // per-parameter (dim-0) layout: every tensor is its own bucket; one
+    // single-bucket launch per non-empty slice
+    for (int64_t b = 0; b < L->nb; ++b) {
+      const int64_t sl = L->bucket_slice(b);
+      if (sl == 0) continue;
+      const int64_t i0 = L->bucket_shard_off(b), f0 = L->bucket_padded_off(b) + r * sl;
+      regs.push_back(Region{i0, sl, sl, sl, 0, f0, 0});
+      vec.push_back(allow_vec && i0 % 8 == 0 && f0 % 8 == 0);
+    }
+  } else if (!map) {
+    regs.push_back(Region{0, S, S, S, 0, 0, 0});
+    vec.push_back(allow_vec);
   } else if (L->nb == 1 || L->s_last == L->s_full) {
     const bool one = L->nb == 1;
-    regs[nreg] = Region{0, S, S, L->s_full, L->p_full, r * L->s_full, 0};
-    vec[nreg++] = allow_vec && (r * L->s_full) % 8 == 0 &&
-                  (one || (L->s_full % 8 == 0 && L->p_full % 8 == 0));
+    regs.push_back(Region{0, S, S, L->s_full, L->p_full, r * L->s_full, 0});
+    vec.push_back(allow_vec && (r * L->s_full) % 8 == 0 &&
+                  (one || (L->s_full % 8 == 0 && L->p_full % 8 == 0)));
   } else {
     const int64_t n0 = (L->nb - 1) * L->s_full;
     const int64_t flat1 = (L->nb - 1) * L->p_full + r * L->s_last;
     const bool v0 = allow_vec && L->s_full % 8 == 0 && L->p_full % 8 == 0;
     const bool v1 = allow_vec && flat1 % 8 == 0;
     if (v0 && v1) {
-      regs[nreg] = Region{0, n0, S, L->s_full, L->p_full, r * L->s_full, flat1};
-      vec[nreg++] = true;
+      regs.push_back(Region{0, n0, S, L->s_full, L->p_full, r * L->s_full, flat1});
+      vec.push_back(true);
     } else if (v0) {
-      regs[nreg] = Region{0, n0, n0, L->s_full, L->p_full, r * L->s_full, 0};
-      vec[nreg++] = true;
-      regs[nreg] = Region{n0, L->s_last, L->s_last, L->s_last, L->p_last, flat1, 0};
-      vec[nreg++] = false;
+      regs.push_back(Region{0, n0, n0, L->s_full, L->p_full, r * L->s_full, 0});
+      vec.push_back(true);
+      regs.push_back(Region{n0, L->s_last, L->s_last, L->s_last, L->p_last, flat1, 0});
+      vec.push_back(false);
     } else {
-      regs[nreg] = Region{0, n0, S, L->s_full, L->p_full, r * L->s_full, flat1};
-      vec[nreg++] = false;
+      regs.push_back(Region{0, n0, S, L->s_full, L->p_full, r * L->s_full, flat1});
+      vec.push_back(false);
     }
   }
 
-  for (int k = 0; k < nreg; ++k) {
+  for (size_t k = 0; k < regs.size(); ++k) {
     const Region& R = regs[k];
     if (R.n <= 0) continue;
     int rc;

@@ -86,6 +86,28 @@ typedef struct zero_layout zero_layout;
  * ZERO_ERANGE (rank out of range or Psi overflows int64). */
 int zero_layout_create(const int64_t* numel, int32_t n_tensors, int64_t bucket_cap, int32_t n_d,
                        int32_t rank, zero_layout** out);
+/* FSDP2 per-parameter layout ("Fully Sharded Data Parallel (FSDP)", "FSDP2":
+ * every parameter is split along dim 0 on its own; the local piece keeps the
+ * parameter's trailing dimensions; the figure shows three (4, 2) weights over
+ * 2 ranks as local (2, 2) pieces, the text an (8, 4) weight over 4 ranks as
+ * local (2, 4)).
+ *
+ * Tensor t has numel[t] elements in rows[t] rows (numel[t] % rows[t] == 0;
+ * rows[t] == 0 only for an empty tensor).  With c_t = ceil(rows[t] / n_d),
+ * rank r owns rows [r*c_t, (r+1)*c_t) of every tensor; rows past rows[t] are
+ * zero padding.  Each tensor is one bucket: padded length n_d*c_t*row_numel,
+ * slice c_t*row_numel; the shard is the slices in tensor order and the
+ * flat (All-Gather) buffer holds every tensor padded to n_d*c_t rows.  All
+ * bucket and tensor queries below apply (bucket b is tensor b).
+ * Errors: ZERO_EINVAL (null, n_d out of range, a row count that does not
+ * divide numel), ZERO_ERANGE (rank out of range, Psi overflow). */
+int zero_layout_create_dim0(const int64_t* numel, const int64_t* rows, int32_t n_tensors,
+                            int32_t n_d, int32_t rank, zero_layout** out);
+
+/* 0 for the bucketed flat layout, 1 for the per-parameter (dim-0) layout,
+ * -1 for a null layout. */
+int32_t zero_layout_kind(const zero_layout* layout);
+
 void zero_layout_destroy(zero_layout* layout);
 
 /* Sizes: Psi (sum of numel), P (padded flat length), S (shard length),

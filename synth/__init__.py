@@ -22,7 +22,7 @@ _lib = None
 DISTS = {"zero": 0, "normal": 1, "absnormal": 2, "student_t3": 3, "normal_zeros": 4}
 OUT_F32, OUT_BF16 = 0, 1
 KIND = {"grad": 1, "master": 2, "exp_avg": 3, "exp_avg_sq": 4, "micro_grad": 5}
-WORKLOAD_ID = {name: k + 1 for k, name in enumerate(workloads.NAMES)}
+WORKLOAD_ID = {name: k + 1 for k, name in enumerate(workloads.NAMES + workloads.DIM0_NAMES)}
 # the padded-tail cut of the 70B list draws the same values as the plain cut
 WORKLOAD_ID["llama70b_t"] = WORKLOAD_ID["llama70b"]
 HOST_THREADS = max(1, min(16, os.cpu_count() or 1))

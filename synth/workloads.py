@@ -13,6 +13,10 @@ and value distributions of the five shard workloads:
              N_d = 64, ZeRO-3 in-place output
   llama70b_t the same list cut into 12,500,000-element buckets, which leaves a
              zero-padded tail in every bucket slice of the last rank
+  gpt2s_fsdp2    GPT-2-small list in the per-parameter dim-0 layout, N_d = 8
+                 (the 50257-row embedding leaves padding rows on the last rank)
+  llama8b_fsdp2  Llama-3-8B list in the per-parameter dim-0 layout, N_d = 8,
+                 ZeRO-3 in place
 
 Distributions are named (kind, scale): "normal" N(0, scale) with scale the
 standard deviation, "absnormal" |N(0, scale)|, "student_t3" Student-t with 3
@@ -90,6 +94,7 @@ class Workload:
     hp: dict = field(default_factory=lambda: dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8,
                                                   weight_decay=0.1))
     shapes: list = None
+    rows: list = None   # per-tensor dim-0 sizes: the per-parameter (FSDP2) layout
 
     @property
     def psi(self):
@@ -128,7 +133,18 @@ def get(name: str) -> Workload:
         return Workload(name, numel_of(sh), cap, 64, 63, "compact", "shard", 1001, 1,
                         ("normal_zeros", 1e-3), ("normal", 0.02), ("normal", 1e-4),
                         ("absnormal", 1e-6), shapes=sh)
+    if name == "gpt2s_fsdp2":
+        sh = gpt2_small_shapes()
+        return Workload(name, numel_of(sh), 0, 8, 7, "flat", "ag_slot", 1, 3,
+                        ("normal", 1e-3), ("normal", 0.02), ("zero", 0.0), ("zero", 0.0),
+                        shapes=sh, rows=[s[1][0] for s in sh])
+    if name == "llama8b_fsdp2":
+        sh = _llama8b()
+        return Workload(name, numel_of(sh), 0, 8, 7, "compact", "shard", 1, 2,
+                        ("student_t3", 1e-3), ("normal", 0.02), ("zero", 0.0), ("zero", 0.0),
+                        shapes=sh, rows=[s[1][0] for s in sh])
     raise KeyError(name)
 
 
 NAMES = ("flat1m", "gpt2s", "accum1p3b", "llama8b", "llama70b", "llama70b_t")
+DIM0_NAMES = ("gpt2s_fsdp2", "llama8b_fsdp2")

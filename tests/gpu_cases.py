@@ -78,8 +78,8 @@ class Case:
 
     def __init__(self, w: workloads.Workload, sample_idx=None):
         self.w = w
-        self.pl = oracle.plan(w.numel, w.cap, w.n_d)
-        self.L = z.Layout(w.numel, w.cap, w.n_d, w.rank)
+        self.pl = oracle.plan(w.numel, w.cap, w.n_d, rows=w.rows)
+        self.L = z.Layout(w.numel, w.cap, w.n_d, w.rank, rows=w.rows)
         self.S, self.P = self.pl.shard_len, self.pl.padded_total
         self.hp_z = z.AdamW(**w.hp)
         self.hp_o = oracle.AdamW(**w.hp)

@@ -87,6 +87,43 @@ def test_layout_agrees_with_oracle_large(name):
         assert (a, b) == (lo[t], hi[t]) or (a == b and lo[t] == hi[t])
 
 
+@pytest.mark.parametrize("seed", range(20))
+def test_dim0_layout_agrees_with_oracle(seed):
+    rng = np.random.default_rng(3000 + seed)
+    n_t = int(rng.integers(1, 8))
+    rows = [int(v) for v in rng.integers(0, 40, n_t)]
+    per_row = [int(v) for v in rng.integers(1, 9, n_t)]
+    numel = [r * k for r, k in zip(rows, per_row)]
+    n_d = int(rng.choice([1, 2, 3, 4, 8, 64]))
+    pl = oracle.plan(numel, 0, n_d, rows=rows)
+    for r in range(n_d):
+        L = z.Layout(numel, 0, n_d, r, rows=rows)
+        assert L.kind == 1
+        assert (L.psi, L.padded, L.shard, L.n_buckets) == (sum(numel), pl.padded_total,
+                                                           pl.shard_len, pl.n_buckets)
+        got = np.array(L.buckets(), dtype=np.int64).reshape(-1, 5)
+        exp = np.stack([pl.stream_off, pl.len, pl.padded_off, pl.padded_len, pl.shard_off], 1)
+        assert np.array_equal(got, exp)
+        lo, hi = pl.tensor_ranges(r)
+        for t in range(n_t):
+            _, a, b = L.tensor(t)
+            assert (a, b) == (lo[t], hi[t]) or (a == b and lo[t] == hi[t])
+
+
+def test_dim0_layout_errors():
+    lib = z.load()
+    h = C.c_void_p()
+    numel = (C.c_int64 * 2)(8, 9)
+    rows = (C.c_int64 * 2)(4, 2)       # 9 is not a multiple of 2
+    assert lib.zero_layout_create_dim0(numel, rows, 2, 2, 0, C.byref(h)) == z.binding.ZERO_EINVAL
+    rows0 = (C.c_int64 * 2)(4, 0)      # zero rows with elements
+    assert lib.zero_layout_create_dim0(numel, rows0, 2, 2, 0, C.byref(h)) == z.binding.ZERO_EINVAL
+    ok = (C.c_int64 * 2)(4, 3)
+    assert lib.zero_layout_create_dim0(numel, ok, 2, 2, 2, C.byref(h)) == z.binding.ZERO_ERANGE
+    assert lib.zero_layout_create_dim0(numel, ok, 2, 0, 0, C.byref(h)) == z.binding.ZERO_EINVAL
+    assert z.Layout([8, 9], 0, 2, 0).kind == 0
+
+
 @pytest.mark.parametrize("t", [1, 2, 10, 101, 1001, 10 ** 6])
 @pytest.mark.parametrize("hp", [dict(), dict(lr=3e-4, beta1=0.8, beta2=0.999, eps=1e-6,
                                              weight_decay=0.0), dict(beta1=0.0, beta2=0.0)])

@@ -659,3 +659,102 @@ def test_reshard_gpt2s_state_8_to_4_ranks_round_trip():
         z.zero_reshard(Ld[0], mid, Ls[r], back)
         torch.cuda.synchronize()
         assert_bitwise(back.cpu().numpy(), src_h[r], f"round trip rank {r}")
+
+
+# ------------------------------------------------------------------ FSDP2 per-parameter layout
+def test_gpt2s_fsdp2_steps_full():
+    """GPT-2-small list sharded per parameter along dim 0 over 8 ranks (the
+    50257-row embedding leaves 7 padding rows on rank 7), FLAT contributions
+    via pack, All-Gather slot output, 3 steps, every element compared."""
+    case = Case(workloads.get("gpt2s_fsdp2"))
+    stats = run_steps(case, full_check_steps=(1,))
+    assert stats["master"] == case.S
+
+
+DIM0_EDGE = [
+    # shapes, n_d, rank, grad_layout, out_mode
+    ([(4, 2), (4, 2), (4, 2)], 2, 1, "flat", "ag_slot"),
+    ([(8, 4)], 4, 2, "compact", "shard"),
+    ([(5, 3), (7,), (1, 9), (16, 16)], 4, 3, "flat", "ag_slot"),
+    ([(5, 3), (7,), (1, 9), (16, 16)], 4, 0, "compact", "ag_slot"),
+    ([(100, 24), (3, 8), (64, 64)], 8, 7, "flat", "shard"),
+    ([(129, 64), (1000,)], 64, 63, "compact", "shard"),
+    ([(129, 64), (1000,), (2, 3)], 64, 5, "flat", "ag_slot"),
+    ([(33, 17), (1,), (250, 40)], 3, 2, "flat", "ag_slot"),
+]
+
+
+@pytest.mark.parametrize("shapes,n_d,rank,gl,om", DIM0_EDGE)
+def test_dim0_layout_steps_full_compare(shapes, n_d, rank, gl, om):
+    numel = [int(np.prod(s)) for s in shapes]
+    w = workloads.Workload("gpt2s_fsdp2", numel, 0, n_d, rank, gl, om, 1, 1, ("normal", 1e-3),
+                           ("normal", 0.02), ("normal", 1e-4), ("absnormal", 1e-6),
+                           rows=[s[0] for s in shapes])
+    case = Case(w)
+    say(f"  dim0 shapes={shapes} n_d={n_d} r={rank} {gl} {om}: S={case.S}")
+    case.init_state_gpu()
+    case.init_state_oracle()
+    for t in (1, 2):
+        case.step_gpu(t, case.grads_gpu(t))
+        case.step_oracle(t, case.grads_oracle(t))
+    torch.cuda.synchronize()
+    case.compare("dim0")
+    for a, b in ((case.master, case.o_master), (case.m, case.o_m), (case.v, case.o_v)):
+        assert_bitwise(a.cpu().numpy(), b, "state")
+    pos = case.flat_pos if om == "ag_slot" else np.arange(case.S)
+    assert_bitwise(u16(case.pout)[pos], case.o_p, "param")
+    case.check_canaries(n_probe=4096)
+
+
+@pytest.mark.timeout(600)
+def test_llama8b_fsdp2_sampled():
+    w = workloads.get("llama8b_fsdp2")
+    case = Case(w)
+    case.__init__(w, sample_idx=sample_indices(case.S, case.pl))
+    run_steps(case)
+
+
+@pytest.mark.parametrize("shapes,n_d", [([(5, 3), (7,), (1, 9), (16, 16)], 4),
+                                        ([(129, 64), (1000,), (2, 3)], 64),
+                                        ([(4, 2), (4, 2), (4, 2)], 2)])
+def test_dim0_gather_and_reshard(shapes, n_d):
+    numel = [int(np.prod(s)) for s in shapes]
+    rows = [s[0] for s in shapes]
+    pd0 = oracle.plan(numel, 0, n_d, rows=rows)
+    sh_h = _rank_shards_bf16(pd0, n_d, 3)
+    sh = [torch.from_numpy(x.view(np.int16)).to(DEV) for x in sh_h]
+    L0 = z.Layout(numel, 0, n_d, 0, rows=rows)
+    out = torch.full((pd0.padded_total,), CANARY, dtype=torch.int16, device=DEV)
+    z.zero_gather_params(L0, sh, out)
+    torch.cuda.synchronize()
+    assert_bitwise(u16(out), oracle.gather(sh_h, pd0), "dim0 gather")
+    # re-cut dim0 -> bucketed -> dim0 (fp32), each piece against the oracle
+    sh32_h = [synth.fill_host(pd0.shard_len, synth.OUT_F32,
+                              synth.shard_segments(pd0.stream_off, pd0.len, pd0.padded_len,
+                                                   pd0.shard_off, n_d, q),
+                              synth.key("gpt2s", "exp_avg_sq"), "absnormal", 1e-6)
+              for q in range(n_d)]
+    sh32 = [torch.from_numpy(x).to(DEV) for x in sh32_h]
+    pb = oracle.plan(numel, 7, 3)
+    mid, mid_h = [], []
+    for r in range(3):
+        o = torch.full((pb.shard_len,), 5.0, dtype=torch.float32, device=DEV)
+        z.zero_reshard(L0, sh32, z.Layout(numel, 7, 3, r), o)
+        mid.append(o)
+        mid_h.append(oracle.reshard(sh32_h, pd0, pb, r))
+    torch.cuda.synchronize()
+    for a, b in zip(mid, mid_h):
+        assert_bitwise(a.cpu().numpy(), b, "dim0 -> bucketed")
+    for r in range(n_d):
+        o = torch.full((pd0.shard_len,), 5.0, dtype=torch.float32, device=DEV)
+        z.zero_reshard(z.Layout(numel, 7, 3, 0), mid, z.Layout(numel, 0, n_d, r, rows=rows), o)
+        torch.cuda.synchronize()
+        assert_bitwise(o.cpu().numpy(), sh32_h[r], f"bucketed -> dim0 rank {r}")
+    # dim0 -> dim0 with another rank count
+    n2 = max(1, n_d // 2)
+    pd2 = oracle.plan(numel, 0, n2, rows=rows)
+    for r in range(n2):
+        o = torch.full((pd2.shard_len,), 5.0, dtype=torch.float32, device=DEV)
+        z.zero_reshard(L0, sh32, z.Layout(numel, 0, n2, r, rows=rows), o)
+        torch.cuda.synchronize()
+        assert_bitwise(o.cpu().numpy(), oracle.reshard(sh32_h, pd0, pd2, r), "dim0 -> dim0")
