@@ -132,13 +132,9 @@ def cpu_baseline(w, segs, S, target_s=12.0):
             "gbps": n * reps * (2 * w.n_d + 26) / dt / 1e9}
 
 
-def aux_kernels(z, synth, workloads):
-    """Pack (gpt2s list, one rank's 124M-element flat buffer) and the no_sync
-    accumulate sequence (accum1p3b shard: 4 calls) timed with HIP events."""
+def make_timer(stream):
+    """fn -> average milliseconds per call (HIP events on `stream`, one untimed call first)."""
     import torch
-    dev = torch.device("cuda:0")
-    out = []
-    stream = torch.cuda.current_stream()
 
     def timed(fn, reps=10):
         fn()
@@ -151,6 +147,18 @@ def aux_kernels(z, synth, workloads):
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
+    return timed
+
+
+def aux_kernels(z, synth, workloads):
+    """Pack (gpt2s list, one rank's 124M-element flat buffer) and the no_sync
+    accumulate sequence (accum1p3b shard: 4 calls) timed with HIP events."""
+    import torch
+    dev = torch.device("cuda:0")
+    out = []
+    stream = torch.cuda.current_stream()
+
+    timed = make_timer(stream)
 
     w = workloads.get("gpt2s")
     L = z.Layout(w.numel, w.cap, w.n_d, w.rank)
@@ -190,6 +198,62 @@ def aux_kernels(z, synth, workloads):
                 "bytes_per_call": nbytes, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
                 "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
     del acc, micro, emit
+    torch.cuda.empty_cache()
+    return out
+
+
+def next_rows(z, synth, w, L, grads, state, pout, timed):
+    """The rows beyond the bf16 step, measured on the same llama8b-sized
+    buffers: FSDP2 (dim-0) step, parameter gather, fp32-contribution step and
+    the 8 -> 4 rank state re-cut.  Consumes `grads` (freed here)."""
+    import torch
+    dev = torch.device("cuda:0")
+    S, P = L.shard, L.padded
+    hp = z.AdamW(**w.hp)
+    out = []
+
+    def row(name, kernel, desc, nbytes, ms):
+        out.append({"row": name, "kernel": kernel, "workload": desc, "bytes_per_call": nbytes,
+                    "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
+                    "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
+
+    master, m, v = state
+    # FSDP2 per-parameter layout, ZeRO-3 in place (COMPACT contributions)
+    rows = [sh[1][0] for sh in w.shapes]
+    Ld = z.Layout(w.numel, 0, w.n_d, w.rank, rows=rows)
+    assert Ld.shard == S
+    shard_out = pout[:S]
+    ms = timed(lambda: z.zero_shard_step(Ld, hp, 5, grads, z.GRAD_COMPACT, master, m, v,
+                                         shard_out, z.OUT_SHARD))
+    row("fsdp2_step", "step_vec_kernel", "llama8b_fsdp2: Llama-3-8B per-parameter dim-0 "
+        "layout, N_d=8, rank 7, in place", S * (2 * w.n_d + 26), ms)
+    # All-Gather local part: the 8 bf16 shards (the contribution buffers
+    # stand in for them) into the 8.03e9-element flat buffer
+    ms = timed(lambda: z.zero_gather_params(L, grads, pout))
+    row("gather", "gather_vec_kernel", "llama8b: 8 rank shards -> 8,030,261,248-element flat "
+        "buffer", 4 * P, ms)
+    del grads[:]
+    torch.cuda.empty_cache()
+    # fp32 contributions
+    g32 = []
+    so, ln, _, pln, sh = (list(x) for x in zip(*L.buckets()))
+    segs = synth.shard_segments(so, ln, pln, sh, w.n_d, w.rank)
+    for q in range(w.n_d):
+        g = torch.empty(S, dtype=torch.float32, device=dev)
+        synth.fill_device(g, segs, synth.key(w.name, "grad", q, 0, w.t_first), *w.grad)
+        g32.append(g)
+    ms = timed(lambda: z.zero_shard_step(L, hp, 7, g32, z.GRAD_COMPACT, master, m, v, pout,
+                                         z.OUT_AG_SLOT))
+    row("step_f32", "step_vec_kernel (fp32 contributions)", "llama8b with fp32 contributions "
+        "(4*N_d+26 = 58 B/elem)", S * (4 * w.n_d + 26), ms)
+    # re-cut one fp32 state array saved from 8 ranks for 4 ranks (the fp32
+    # buffers stand in for the 8 saved shards)
+    L4 = z.Layout(w.numel, w.cap, 4, 3)
+    dst = torch.empty(L4.shard, dtype=torch.float32, device=dev)
+    ms = timed(lambda: z.zero_reshard(L, g32, L4, dst), reps=5)
+    row("reshard", "reshard_kernel<u32>", "llama8b fp32 state: 8 ranks -> rank 3 of 4 "
+        f"({L4.shard} elements)", 8 * L4.shard, ms)
+    del g32, dst
     torch.cuda.empty_cache()
     return out
 
@@ -279,12 +343,15 @@ def main():
     ceil_gbps, ceil_cfg = measure.stream_ceiling(grads, [master, m, v], pout, S)
     print(f"# same-mix streaming ceiling: {ceil_gbps:.0f} GB/s {ceil_cfg}", file=sys.stderr,
           flush=True)
+    nxt = []
+    if not args.no_aux and w.name == "llama8b":
+        nxt = next_rows(z, synth, w, L, grads, [master, m, v], pout, make_timer(stream))
     del grads
     torch.cuda.empty_cache()
-    aux = [] if args.no_aux else aux_kernels(z, synth, workloads)
+    aux = nxt + ([] if args.no_aux else aux_kernels(z, synth, workloads))
     for a in aux:
-        print(f"# {a['kernel']}: {a['ms']:.3f} ms, {a['GBps']:.0f} GB/s", file=sys.stderr,
-              flush=True)
+        print(f"# {a.get('row', a['kernel'])}: {a['ms']:.3f} ms, {a['GBps']:.0f} GB/s "
+              f"({100 * a['frac']:.1f} % of 8 TB/s)", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, segs, S)

@@ -9,7 +9,6 @@ is the planted mistake's doing, not the harness's).
 import contextlib
 import os
 import subprocess
-import tempfile
 from concurrent.futures import ThreadPoolExecutor
 
 import pytest
@@ -142,10 +141,10 @@ def compile_variant(src_text, out_path):
 
 
 @pytest.fixture(scope="module")
-def variants():
+def variants(tmp_path_factory):
     """Compile the unmutated oracle and every mutant (in parallel)."""
     src = open(SRC).read()
-    tmp = tempfile.mkdtemp(prefix="oracle_mut_")
+    tmp = str(tmp_path_factory.mktemp("oracle_mut"))
     jobs = [("control", src, os.path.join(tmp, "control.so"))]
     for k, (name, old, new, _) in enumerate(MUTATIONS):
         assert src.count(old) == 1, f"mutation site not unique or missing: {name}"
