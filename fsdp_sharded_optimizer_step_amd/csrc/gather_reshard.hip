@@ -53,60 +53,54 @@ __device__ __forceinline__ int64_t real_len(const Geo& g, int64_t b) {
 }
 
 // ------------------------------------------------------------------ gather
+// A launch covers a run of buckets with one slice length.  The copy is cut
+// into (bucket, rank, tile) work items, one per block: the block finds its
+// item with a few uniform integer divisions and then copies a contiguous
+// tile of the rank's slice into the bucket's slot q -- no per-element index
+// arithmetic.
 struct GatherArgs {
-  const uint16_t* shard[ZERO_MAX_ND];
-  uint16_t* out;
-  Geo g;
-  int64_t f0, f1;  // flat range [f0, f1) = buckets [b0, b1)
+  const uint16_t* shard[ZERO_MAX_ND];  // each rank's shard, at the run's first bucket
+  uint16_t* out;                       // flat buffer, at the run's first bucket
+  int64_t slice;                       // slice length of every bucket of the run
+  int64_t sstride, pstride;            // shard / flat distance between buckets of the run
+  uint32_t tiles;                      // tiles per slice
+  int32_t n_d;
 };
+constexpr int kGatherThreads = 256;
+constexpr int64_t kGatherTile = kGatherThreads * 8 * 4;  // elements per tile
 
-// Flat position f -> (bucket, rank q, offset j in the slice).
-__device__ __forceinline__ void split_flat(const Geo& g, int64_t f, int64_t& b, int32_t& q,
-                                           int64_t& j) {
-  b = f / g.p_full;
-  if (b >= g.nb) b = g.nb - 1;
-  const int64_t w = f - b * g.p_full;
-  const int64_t sb = slice_len(g, b);
-  q = (int32_t)(w / sb);
-  j = w - (int64_t)q * sb;
-}
-
-// Vector path: every slice length is a multiple of 8 and every base is
-// 16-byte aligned, so 8 consecutive flat elements come from one shard.
-__global__ void __launch_bounds__(256) gather_vec_kernel(const GatherArgs A) {
-  const int64_t nv = (A.f1 - A.f0) >> 3;
-  const int64_t T = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nv; v += T) {
-    const int64_t f = A.f0 + (v << 3);
-    int64_t b, j;
-    int32_t q;
-    split_flat(A.g, f, b, q, j);
-    const u32x4 x = ld_stream<false>((const u32x4*)(A.shard[q] + b * A.g.s_full + j));
-    st_stream<false>((u32x4*)(A.out + f), x);
-  }
-}
-
-__global__ void __launch_bounds__(256) gather_scalar_kernel(const GatherArgs A) {
-  const int64_t n = A.f1 - A.f0;
-  const int64_t T = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += T) {
-    const int64_t f = A.f0 + e;
-    int64_t b, j;
-    int32_t q;
-    split_flat(A.g, f, b, q, j);
-    A.out[f] = A.shard[q][b * A.g.s_full + j];
+template <bool VEC>
+__global__ void __launch_bounds__(kGatherThreads) gather_kernel(const GatherArgs A) {
+  const uint32_t item = blockIdx.x;
+  const uint32_t s = item / A.tiles;             // slice number = bucket * n_d + rank
+  const uint32_t c = item - s * A.tiles;         // tile within the slice
+  const uint32_t b = s / (uint32_t)A.n_d;
+  const uint32_t q = s - b * (uint32_t)A.n_d;
+  const uint16_t* src = A.shard[q] + (int64_t)b * A.sstride;
+  uint16_t* dst = A.out + (int64_t)b * A.pstride + (int64_t)q * A.slice;
+  const int64_t e0 = (int64_t)c * kGatherTile;
+  const int64_t e1 = e0 + kGatherTile < A.slice ? e0 + kGatherTile : A.slice;
+  if constexpr (VEC) {
+    // slice % 8 == 0 and 16-byte aligned bases: whole vectors only
+    const u32x4* sv = (const u32x4*)(src + e0);
+    u32x4* dv = (u32x4*)(dst + e0);
+    const int64_t nv = (e1 - e0) >> 3;
+    for (int64_t v = threadIdx.x; v < nv; v += kGatherThreads)
+      st_stream<false>(dv + v, ld_stream<false>(sv + v));
+  } else {
+    for (int64_t e = e0 + threadIdx.x; e < e1; e += kGatherThreads) dst[e] = src[e];
   }
 }
 
 // ------------------------------------------------------------------ reshard
 // One launch covers the destination shard indices [i0, i0 + n).  The
-// destination index i maps to the stream position
-//   x = d_base_x + stream_of(gd, i - d_base_i)     (or padding)
-// and, when has_src, the source element is found by
-//   locate(gs, x - s_base_x)   if 0 <= x - s_base_x < s_len
-// in the source shards (pointers already shifted to the source bucket).
-// Padding is written as zero when zero_pads; positions whose stream element
-// lies outside this launch's source range are left alone.
+// destination index i maps, through geometry gd taken at origin d_base_i,
+// to the stream position x = d_base_x + (position in gd), or to padding;
+// when has_src, the source element of x is found through geometry gs at
+// stream origin s_base_x, if 0 <= x - s_base_x < s_len, in the source shards
+// (pointers already shifted to the source bucket).  Padding is written as
+// zero when zero_pads; positions whose stream element lies outside this
+// launch's source range are left alone.
 struct ReshardArgs {
   const void* src[ZERO_MAX_ND];
   void* dst;
@@ -115,51 +109,100 @@ struct ReshardArgs {
   int32_t zero_pads, has_src;
 };
 
-// Destination shard index -> stream position (or -1 for padding).
-__device__ __forceinline__ int64_t stream_of(const Geo& g, int64_t i) {
+// Destination index i (relative to the geometry) -> stream position x (or
+// -1 for padding) and the number of following indices, this one included,
+// whose positions continue the same run (consecutive stream positions, or
+// padding).
+struct Run {
+  int64_t x, rem;
+};
+__device__ __forceinline__ Run dst_run(const Geo& g, int64_t i) {
   int64_t b = g.s_full > 0 ? i / g.s_full : 0;
   if (b >= g.nb) b = g.nb - 1;
   const int64_t j = i - b * g.s_full;
-  const int64_t pos = (int64_t)g.rank * slice_len(g, b) + j;
-  return pos < real_len(g, b) ? b * g.cap + pos : -1;
+  const int64_t sl = slice_len(g, b), len = real_len(g, b);
+  const int64_t pos = (int64_t)g.rank * sl + j;
+  if (pos < len) return Run{b * g.cap + pos, (sl - j) < (len - pos) ? (sl - j) : (len - pos)};
+  return Run{-1, sl - j};
 }
 
-// Stream position -> (source rank, source shard index).
-__device__ __forceinline__ void locate(const Geo& g, int64_t x, int32_t& q, int64_t& idx) {
+// Stream position -> source rank, source shard index, and how many
+// consecutive positions stay in the same source slice.
+struct SrcRun {
+  int64_t idx, rem;
+  int32_t q;
+};
+__device__ __forceinline__ SrcRun src_run(const Geo& g, int64_t x) {
   int64_t b = x / g.cap;
   if (b >= g.nb) b = g.nb - 1;
   const int64_t w = x - b * g.cap;
   const int64_t sb = slice_len(g, b);
-  q = (int32_t)(w / sb);
-  idx = b * g.s_full + (w - (int64_t)q * sb);
+  const int32_t q = (int32_t)(w / sb);
+  const int64_t j = w - (int64_t)q * sb;
+  const int64_t left = real_len(g, b) - w;
+  return SrcRun{b * g.s_full + j, (sb - j) < left ? (sb - j) : left, q};
 }
 
+// Each block takes a tile of consecutive destination indices and walks it
+// in runs that are contiguous on both sides (one destination slice, one
+// source slice); all run arithmetic is uniform across the block, and each
+// run is copied by the whole block, 16 bytes at a time when source and
+// destination share their alignment.
+constexpr int kResThreads = 256;
+constexpr int64_t kResTile = 8192;
+
 template <class T>
-__global__ void __launch_bounds__(256) reshard_kernel(const ReshardArgs A) {
-  const int64_t T_ = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < A.n; e += T_) {
-    const int64_t i = A.i0 + e;
-    const int64_t xl = stream_of(A.gd, i - A.d_base_i);
-    if (xl < 0) {
-      if (A.zero_pads) ((T*)A.dst)[i] = T(0);
-      continue;
-    }
-    if (!A.has_src) continue;
-    const int64_t xs = A.d_base_x + xl - A.s_base_x;
-    if (xs < 0 || xs >= A.s_len) continue;
-    int32_t q;
-    int64_t idx;
-    locate(A.gs, xs, q, idx);
-    ((T*)A.dst)[i] = ((const T*)A.src[q])[idx];
+__device__ __forceinline__ void copy_run(T* dst, const T* src, int64_t n) {
+  const uintptr_t da = (uintptr_t)dst, sa = (uintptr_t)src;
+  if (((da ^ sa) & 15u) == 0) {
+    const int64_t head = std::min<int64_t>(n, (int64_t)(((16u - (da & 15u)) & 15u) / sizeof(T)));
+    if (threadIdx.x < head) dst[threadIdx.x] = src[threadIdx.x];
+    constexpr int per = 16 / sizeof(T);
+    const int64_t nv = (n - head) / per;
+    u32x4* dv = (u32x4*)(dst + head);
+    const u32x4* sv = (const u32x4*)(src + head);
+    for (int64_t v = threadIdx.x; v < nv; v += kResThreads)
+      st_stream<false>(dv + v, ld_stream<false>(sv + v));
+    const int64_t t0 = head + nv * per;
+    if (threadIdx.x < n - t0) dst[t0 + threadIdx.x] = src[t0 + threadIdx.x];
+  } else {
+    for (int64_t k = threadIdx.x; k < n; k += kResThreads) dst[k] = src[k];
   }
 }
 
-int cus() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
-  return n;
+template <class T>
+__device__ __forceinline__ void zero_run(T* dst, int64_t n) {
+  for (int64_t k = threadIdx.x; k < n; k += kResThreads) dst[k] = T(0);
+}
+
+template <class T>
+__global__ void __launch_bounds__(kResThreads) reshard_kernel(const ReshardArgs A) {
+  const int64_t e_begin = (int64_t)blockIdx.x * kResTile;
+  if (e_begin >= A.n) return;
+  const int64_t e_end = std::min(A.n, e_begin + kResTile);
+  T* dst = (T*)A.dst + A.i0;
+  for (int64_t e = e_begin; e < e_end;) {
+    const Run d = dst_run(A.gd, A.i0 + e - A.d_base_i);
+    int64_t len = std::min(d.rem, e_end - e);
+    if (d.x < 0) {
+      if (A.zero_pads) zero_run(dst + e, len);
+      e += len;
+      continue;
+    }
+    const int64_t xs = A.d_base_x + d.x - A.s_base_x;
+    if (!A.has_src || xs >= A.s_len) {
+      e += len;
+      continue;
+    }
+    if (xs < 0) {
+      e += std::min(len, -xs);
+      continue;
+    }
+    const SrcRun sr = src_run(A.gs, xs);
+    len = std::min(len, std::min(sr.rem, A.s_len - xs));
+    copy_run(dst + e, (const T*)A.src[sr.q] + sr.idx, len);
+    e += len;
+  }
 }
 
 bool a16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -168,10 +211,6 @@ bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
   if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
   const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
   return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
-}
-
-int blocks_for(int64_t work) {
-  return (int)std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256, (int64_t)cus() * 4));
 }
 
 }  // namespace
@@ -189,34 +228,45 @@ int zero_gather_params(const zero_layout* L, const uint16_t* const* rank_shards,
     if (overlap(rank_shards[q], 2 * L->S, full_out, 2 * L->P)) return ZERO_EOVERLAP;
   }
   if (bucket_begin == bucket_end) return ZERO_OK;
-  auto launch = [&](const Geo& g, int64_t shard_shift, int64_t out_shift, int64_t f0,
-                    int64_t f1) -> int {
+  // One launch per run of buckets with equal slices: the full buckets of a
+  // bucketed layout, its last bucket, or one tensor of a per-parameter layout.
+  auto launch = [&](int64_t b0, int64_t nbk, int64_t slice, int64_t sstride,
+                    int64_t pstride) -> int {
+    if (nbk <= 0 || slice <= 0) return ZERO_OK;
     GatherArgs A;
+    const int64_t shard0 = L->bucket_shard_off(b0), flat0 = L->bucket_padded_off(b0);
     for (int q = 0; q < ZERO_MAX_ND; ++q)
-      A.shard[q] = q < nd ? rank_shards[q] + shard_shift : nullptr;
-    A.out = full_out + out_shift;
-    A.g = g;
-    A.f0 = f0;
-    A.f1 = f1;
-    bool vec = a16(A.out) && g.s_full % 8 == 0 && g.s_last % 8 == 0 && f0 % 8 == 0;
+      A.shard[q] = q < nd ? rank_shards[q] + shard0 : nullptr;
+    A.out = full_out + flat0;
+    A.slice = slice;
+    A.sstride = sstride;
+    A.pstride = pstride;
+    A.n_d = nd;
+    const int64_t tiles = (slice + kGatherTile - 1) / kGatherTile;
+    const int64_t items = nbk * nd * tiles;
+    if (items > 0x7fffffff) return ZERO_ERANGE;
+    A.tiles = (uint32_t)tiles;
+    bool vec = a16(A.out) && slice % 8 == 0 && pstride % 8 == 0 && sstride % 8 == 0;
     for (int32_t q = 0; q < nd; ++q) vec = vec && a16(A.shard[q]);
     if (vec)
-      hipLaunchKernelGGL(gather_vec_kernel, dim3(blocks_for((f1 - f0) >> 3)), dim3(256), 0,
+      hipLaunchKernelGGL(gather_kernel<true>, dim3((unsigned)items), dim3(kGatherThreads), 0,
                          stream, A);
     else
-      hipLaunchKernelGGL(gather_scalar_kernel, dim3(blocks_for(f1 - f0)), dim3(256), 0, stream,
-                         A);
+      hipLaunchKernelGGL(gather_kernel<false>, dim3((unsigned)items), dim3(kGatherThreads), 0,
+                         stream, A);
     return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
   };
   if (L->fixed()) {
-    const int64_t f0 = L->bucket_padded_off(bucket_begin);
-    const int64_t f1 = L->bucket_padded_off(bucket_end - 1) + L->bucket_padded(bucket_end - 1);
-    return launch(geo_of(*L), 0, 0, f0, f1);
+    const int64_t last = L->nb - 1;
+    const int64_t full_end = std::min(bucket_end, last);
+    int rc = launch(bucket_begin, full_end - bucket_begin, L->s_full, L->s_full, L->p_full);
+    if (rc == ZERO_OK && bucket_end > last && bucket_begin <= last)
+      rc = launch(last, 1, L->s_last, L->s_last, L->p_last);
+    return rc;
   }
   for (int64_t b = bucket_begin; b < bucket_end; ++b) {
-    if (L->bucket_slice(b) == 0) continue;
-    const int rc = launch(geo_of_bucket(*L, b), L->bucket_shard_off(b), L->bucket_padded_off(b),
-                          0, L->bucket_padded(b));
+    const int64_t sl = L->bucket_slice(b);
+    const int rc = launch(b, 1, sl, sl, sl * nd);
     if (rc != ZERO_OK) return rc;
   }
   return ZERO_OK;
@@ -255,10 +305,14 @@ int zero_reshard(const zero_layout* src, const void* const* src_shards, const ze
     A.s_len = s_len;
     A.zero_pads = zero_pads ? 1 : 0;
     A.has_src = gs ? 1 : 0;
+    const int64_t tiles = (n + kResTile - 1) / kResTile;
+    if (tiles > 0x7fffffff) return ZERO_ERANGE;
     if (elem_bytes == 4)
-      hipLaunchKernelGGL(reshard_kernel<uint32_t>, dim3(blocks_for(n)), dim3(256), 0, stream, A);
+      hipLaunchKernelGGL(reshard_kernel<uint32_t>, dim3((unsigned)tiles), dim3(kResThreads), 0,
+                         stream, A);
     else
-      hipLaunchKernelGGL(reshard_kernel<uint16_t>, dim3(blocks_for(n)), dim3(256), 0, stream, A);
+      hipLaunchKernelGGL(reshard_kernel<uint16_t>, dim3((unsigned)tiles), dim3(kResThreads), 0,
+                         stream, A);
     return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
   };
 
