@@ -758,3 +758,69 @@ def test_dim0_gather_and_reshard(shapes, n_d):
         z.zero_reshard(L0, sh32, z.Layout(numel, 0, n2, r, rows=rows), o)
         torch.cuda.synchronize()
         assert_bitwise(o.cpu().numpy(), oracle.reshard(sh32_h, pd0, pd2, r), "dim0 -> dim0")
+
+
+# ------------------------------------------------------------------ graph capture
+def test_hip_graph_capture_of_accumulate_and_step():
+    """The entry points launch kernels only (no allocation, memset or
+    synchronisation), so a no_sync accumulation of 4 micro-batches for 2
+    ranks followed by the shard step can be captured in one HIP graph.  Each
+    of several replays (with eager work and synchronisations in between)
+    equals the same sequence run eagerly, bit for bit."""
+    numel, cap, n_d, rank, t = [700_001, 3_333], 65_536, 2, 1, 9
+    L = z.Layout(numel, cap, n_d, rank)
+    S, P = L.shard, L.padded
+    hp = z.AdamW()
+    rng = np.random.default_rng(31)
+
+    def bf16(n, scale):
+        return torch.from_numpy(oracle.round_bf16((rng.standard_normal(n) * scale)
+                                                  .astype(np.float32)).view(np.int16)).to(DEV)
+
+    micro = [[bf16(S, 2e-3) for _ in range(4)] for _ in range(n_d)]
+    init = [torch.from_numpy((rng.standard_normal(S) * s).astype(np.float32)).to(DEV)
+            for s in (0.02, 1e-4)] + [torch.from_numpy(
+                np.abs(rng.standard_normal(S) * 1e-6).astype(np.float32)).to(DEV)]
+
+    def make_bufs():
+        return dict(acc=torch.zeros(S, dtype=torch.float32, device=DEV),
+                    contrib=[torch.zeros(S, dtype=torch.int16, device=DEV) for _ in range(n_d)],
+                    state=[x.clone() for x in init],
+                    pout=torch.full((P,), CANARY, dtype=torch.int16, device=DEV))
+
+    def sequence(b, stream=None):
+        for q in range(n_d):
+            for k in range(4):
+                last = k == 3
+                flags = (z.ACC_OVERWRITE if k == 0 else 0) | (
+                    z.ACC_EMIT_BF16 | z.ACC_NO_STORE if last else 0)
+                z.zero_grad_accumulate(b["acc"], micro[q][k], 0.25, flags,
+                                       b["contrib"][q] if last else None, stream=stream)
+        z.zero_shard_step(L, hp, t, b["contrib"], z.GRAD_COMPACT, *b["state"], b["pout"],
+                          z.OUT_AG_SLOT, stream=stream)
+
+    eager = make_bufs()
+    expected = []
+    for _ in range(3):
+        sequence(eager)
+        torch.cuda.synchronize()
+        expected.append([x.cpu().numpy() for x in eager["state"]] + [u16(eager["pout"])])
+
+    graphed = make_bufs()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            sequence(graphed, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        junk = torch.ones(1 << 20, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        got = [x.cpu().numpy() for x in graphed["state"]] + [u16(graphed["pout"])]
+        for a, b in zip(got, expected[r]):
+            assert_bitwise(a, b, f"graph replay {r}")
+        del junk
