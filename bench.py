@@ -258,6 +258,60 @@ def next_rows(z, synth, w, L, grads, state, pout, timed):
     return out
 
 
+def all_configs(z, synth, workloads, steps, warmup):
+    """Step time of every shard workload (inputs resident, HIP events on the
+    launch stream); FLAT workloads read their contributions from N_d packed
+    flat buffers, the others from N_d shard-ordered buffers."""
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    timed = make_timer(stream)
+    res = []
+    for name in workloads.NAMES + workloads.DIM0_NAMES:
+        w = workloads.get(name)
+        L = z.Layout(w.numel, w.cap, w.n_d, w.rank, rows=w.rows)
+        S, P = L.shard, L.padded
+        so, ln, _, pln, sh = (list(x) for x in zip(*L.buckets()))
+        segs = synth.shard_segments(so, ln, pln, sh, w.n_d, w.rank)
+        gdist = w.micro_grad if w.n_micro else w.grad
+        grads = []
+        for q in range(w.n_d):
+            if w.grad_layout == "compact":
+                g = torch.empty(S, dtype=torch.int16, device=dev)
+                synth.fill_device(g, segs, synth.key(w.name, "grad", q, 0, w.t_first), *gdist)
+            else:
+                g = torch.empty(P, dtype=torch.int16, device=dev)
+                flat_segs = [(po, s0, l, pl - l) for s0, l, po, pl in
+                             zip(so, ln, [b[2] for b in L.buckets()], pln)]
+                synth.fill_device(g, flat_segs, synth.key(w.name, "grad", q, 0, w.t_first),
+                                  *gdist)
+            grads.append(g)
+        state = []
+        for kind, dist in (("master", w.master), ("exp_avg", w.exp_avg),
+                           ("exp_avg_sq", w.exp_avg_sq)):
+            b = torch.empty(S, dtype=torch.float32, device=dev)
+            synth.fill_device(b, segs, synth.key(w.name, kind), *dist)
+            state.append(b)
+        pout = torch.zeros(P if w.out_mode == "ag_slot" else S, dtype=torch.int16, device=dev)
+        hp = z.AdamW(**w.hp)
+        gl = z.GRAD_COMPACT if w.grad_layout == "compact" else z.GRAD_FLAT
+        om = z.OUT_AG_SLOT if w.out_mode == "ag_slot" else z.OUT_SHARD
+        for _ in range(warmup):
+            z.zero_shard_step(L, hp, w.t_first, grads, gl, *state, pout, om)
+        ms = timed(lambda: z.zero_shard_step(L, hp, w.t_first, grads, gl, *state, pout, om),
+                   reps=steps)
+        nbytes = S * (2 * w.n_d + 26)
+        res.append({"workload": name, "shard_elems": S, "n_d": w.n_d, "buckets": L.n_buckets,
+                    "grad_layout": w.grad_layout, "out_mode": w.out_mode, "ms": ms,
+                    "Gelem_per_s": S / (ms * 1e-3) / 1e9, "GBps": nbytes / (ms * 1e-3) / 1e9,
+                    "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
+        print(f"# {name}: S={S} {ms:.4f} ms {res[-1]['GBps']:.0f} GB/s", file=sys.stderr,
+              flush=True)
+        del grads, state, pout
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,6 +322,8 @@ def main():
     ap.add_argument("--no-aux", action="store_true", help="skip the pack/accumulate timings")
     ap.add_argument("--blocks", type=int, default=0)
     ap.add_argument("--threads", type=int, default=0)
+    ap.add_argument("--all-configs", action="store_true",
+                    help="time the step of every shard workload instead (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (3 times): the known-size "
                          "reference for scaling HBM byte counters")
@@ -294,6 +350,10 @@ def main():
     from synth import workloads
 
     z.load()
+    if args.all_configs:
+        print(json.dumps({"per_config": all_configs(z, synth, workloads, args.steps,
+                                                    args.warmup)}), flush=True)
+        return
     w = workloads.get(args.workload)
     L = z.Layout(w.numel, w.cap, w.n_d, w.rank)
     S, P = L.shard, L.padded
