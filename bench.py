@@ -199,13 +199,64 @@ def aux_kernels(z, synth, workloads):
                 "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
     del acc, micro, emit
     torch.cuda.empty_cache()
+
+    # the whole no_sync step of accum1p3b: every rank accumulates its 4
+    # micro-batches, then the shard step -- the last accumulate as its own
+    # call (emit bf16) or folded into the step (zero_shard_step_accumulate)
+    hp = z.AdamW(**w.hp)
+    accs = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(w.n_d)]
+    micro = [[torch.empty(S, dtype=torch.int16, device=dev) for _ in range(w.n_micro)]
+             for _ in range(w.n_d)]
+    for q in range(w.n_d):
+        for k in range(w.n_micro):
+            synth.fill_device(micro[q][k], segs, synth.key(w.name, "micro_grad", q, k, w.t_first),
+                              *w.micro_grad)
+    contribs = [torch.empty(S, dtype=torch.int16, device=dev) for _ in range(w.n_d)]
+    state = [torch.zeros(S, dtype=torch.float32, device=dev) for _ in range(3)]
+    pout = torch.empty(L.padded, dtype=torch.int16, device=dev)
+    scale = 1.0 / w.n_micro
+
+    def job(fused):
+        for q in range(w.n_d):
+            for k in range(w.n_micro - (1 if fused else 0)):
+                last = k == w.n_micro - 1
+                flags = (z.ACC_OVERWRITE if k == 0 else 0) | (
+                    z.ACC_EMIT_BF16 | z.ACC_NO_STORE if last else 0)
+                z.zero_grad_accumulate(accs[q], micro[q][k], scale, flags,
+                                       contribs[q] if last else None)
+        if fused:
+            z.zero_shard_step_accumulate(L, hp, w.t_first, accs, [mq[-1] for mq in micro], scale,
+                                         z.DTYPE_BF16, z.GRAD_COMPACT, *state, pout,
+                                         z.OUT_AG_SLOT)
+        else:
+            z.zero_shard_step(L, hp, w.t_first, contribs, z.GRAD_COMPACT, *state, pout,
+                              z.OUT_AG_SLOT)
+
+    nd, nm = w.n_d, w.n_micro
+    for fused in (False, True):
+        ms = timed(lambda: job(fused), reps=3)
+        if fused:
+            nbytes = S * (nd * (6 + 10 * (nm - 2)) + 6 * nd + 26)
+            desc = (f"accum1p3b job: {nd} ranks x {nm - 1} accumulate calls, then the step "
+                    "folding in each rank's last micro-batch (6*N_d+26 B/elem)")
+        else:
+            nbytes = S * (nd * (6 + 10 * (nm - 2) + 8) + 2 * nd + 26)
+            desc = (f"accum1p3b job: {nd} ranks x {nm} accumulate calls (last emits bf16), "
+                    "then the step")
+        out.append({"kernel": "accum_vec_kernel + step_vec_kernel" + (" (fused)" if fused else ""),
+                    "workload": desc, "bytes_per_call": nbytes, "ms": ms,
+                    "GBps": nbytes / (ms * 1e-3) / 1e9,
+                    "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
+    del accs, micro, contribs, state, pout
+    torch.cuda.empty_cache()
     return out
 
 
 def next_rows(z, synth, w, L, grads, state, pout, timed):
     """The rows beyond the bf16 step, measured on the same llama8b-sized
-    buffers: FSDP2 (dim-0) step, parameter gather, fp32-contribution step and
-    the 8 -> 4 rank state re-cut.  Consumes `grads` (freed here)."""
+    buffers: FSDP2 (dim-0) step, parameter gather, fp32-contribution step,
+    the step with the last micro-batch folded in and the 8 -> 4 rank state
+    re-cut.  Consumes `grads` (freed here)."""
     import torch
     dev = torch.device("cuda:0")
     S, P = L.shard, L.padded
@@ -246,6 +297,21 @@ def next_rows(z, synth, w, L, grads, state, pout, timed):
                                          z.OUT_AG_SLOT))
     row("step_f32", "step_vec_kernel (fp32 contributions)", "llama8b with fp32 contributions "
         "(4*N_d+26 = 58 B/elem)", S * (4 * w.n_d + 26), ms)
+    # the last no_sync micro-batch folded into the step: the fp32 buffers
+    # stand in for the ranks' accumulators, plus one bf16 micro-batch each
+    micro = []
+    for q in range(w.n_d):
+        g = torch.empty(S, dtype=torch.int16, device=dev)
+        synth.fill_device(g, segs, synth.key(w.name, "grad", q, 1, w.t_first), *w.grad)
+        micro.append(g)
+    ms = timed(lambda: z.zero_shard_step_accumulate(L, hp, 8, g32, micro, 0.25, z.DTYPE_BF16,
+                                                    z.GRAD_COMPACT, master, m, v, pout,
+                                                    z.OUT_AG_SLOT))
+    row("step_fused_accumulate", "step_vec_kernel (accumulator + last micro-batch)",
+        "llama8b, each rank's contribution = bf16(acc + micro/4) inside the step "
+        "(6*N_d+26 = 74 B/elem)", S * (6 * w.n_d + 26), ms)
+    del micro
+    torch.cuda.empty_cache()
     # re-cut one fp32 state array saved from 8 ranks for 4 ranks (the fp32
     # buffers stand in for the 8 saved shards)
     L4 = z.Layout(w.numel, w.cap, 4, 3)

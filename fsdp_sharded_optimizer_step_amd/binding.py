@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libzero_shard.so")
 
 ZERO_OK, ZERO_EINVAL, ZERO_ERANGE, ZERO_EHIP, ZERO_EOVERLAP = 0, -1, -3, -4, -5
 ZERO_MAX_ND = 256
+ZERO_MAX_ND_FUSED = 128
 GRAD_COMPACT, GRAD_FLAT = 0, 1
 OUT_AG_SLOT, OUT_SHARD = 0, 1
 ACC_OVERWRITE, ACC_EMIT_BF16, ACC_NO_STORE = 1, 2, 4
@@ -25,7 +26,8 @@ EXPORTS = ("zero_layout_create", "zero_layout_destroy", "zero_layout_psi", "zero
            "zero_layout_shard", "zero_layout_n_buckets", "zero_layout_n_d", "zero_layout_rank",
            "zero_layout_bucket", "zero_layout_tensor", "zero_bucket_pack", "zero_grad_accumulate",
            "zero_shard_step", "zero_shard_step_ex", "zero_step_scalars", "zero_strerror",
-           "zero_gather_params", "zero_reshard", "zero_layout_create_dim0", "zero_layout_kind")
+           "zero_gather_params", "zero_reshard", "zero_layout_create_dim0", "zero_layout_kind",
+           "zero_shard_step_accumulate")
 
 
 class ZeroError(RuntimeError):
@@ -85,6 +87,10 @@ def load():
     lib.zero_shard_step_ex.argtypes = [vp, C.POINTER(_AdamW), C.c_int64, C.POINTER(vp),
                                        C.c_int32, vp, vp, vp, vp, C.c_int32, vp,
                                        C.POINTER(_Options), vp]
+    lib.zero_shard_step_accumulate.argtypes = [vp, C.POINTER(_AdamW), C.c_int64, C.POINTER(vp),
+                                               C.POINTER(vp), C.c_float, C.c_int32, C.c_int32,
+                                               vp, vp, vp, vp, C.c_int32, vp,
+                                               C.POINTER(_Options), vp]
     lib.zero_gather_params.argtypes = [vp, C.POINTER(vp), C.c_int64, C.c_int64, vp, vp]
     lib.zero_reshard.argtypes = [vp, C.POINTER(vp), vp, vp, C.c_int32, vp]
     lib.zero_step_scalars.argtypes = [C.POINTER(_AdamW), C.c_int64, C.POINTER(C.c_float)]
@@ -242,6 +248,25 @@ def zero_shard_step(layout: Layout, hp: AdamW, t: int, rank_grads, grad_layout: 
         opt = _Options(DTYPE_F32 if f32 else DTYPE_BF16, blocks, threads, path)
         _check("zero_shard_step_ex", load().zero_shard_step_ex(*args, C.byref(opt),
                                                                 _stream_ptr(stream)))
+
+
+def zero_shard_step_accumulate(layout: Layout, hp: AdamW, t: int, rank_acc, rank_micro,
+                               micro_scale: float, contrib_dtype: int, grad_layout: int, master,
+                               exp_avg, exp_avg_sq, param_out, out_mode: int,
+                               reduced_grad_out=None, stream=None, launch=None):
+    """One shard step whose contributions are the ranks' fp32 accumulators
+    plus their scaled last micro-batch (rounded to bf16 for DTYPE_BF16)."""
+    if len(rank_acc) != layout.n_d or len(rank_micro) != layout.n_d:
+        raise ValueError("zero_shard_step_accumulate: one accumulator and one micro-batch "
+                         "gradient per rank are required")
+    blocks, threads, path = launch if launch is not None else (0, 0, 0)
+    opt = _Options(contrib_dtype, blocks, threads, path)
+    _check("zero_shard_step_accumulate", load().zero_shard_step_accumulate(
+        layout.handle, C.byref(hp._c()), int(t), _ptr_array(rank_acc, "rank_acc", _dev32),
+        _ptr_array(rank_micro, "rank_micro"), float(micro_scale), contrib_dtype, grad_layout,
+        _dev32(master, "master"), _dev32(exp_avg, "exp_avg"), _dev32(exp_avg_sq, "exp_avg_sq"),
+        _dev16(param_out, "param_out"), out_mode, _dev32(reduced_grad_out, "reduced_grad_out"),
+        C.byref(opt), _stream_ptr(stream)))
 
 
 def zero_gather_params(layout: Layout, rank_shards, full_out, bucket_begin: int = 0,

@@ -1,25 +1,29 @@
-// zero_shard_step: rank-ordered reduction of N_d bf16 contributions, AdamW on
-// the fp32 master/m/v shard, bf16 cast and slot (or in-place) store -- one
-// streaming pass over the shard.
+// zero_shard_step: rank-ordered reduction of N_d gradient contributions,
+// AdamW on the fp32 master/m/v shard, bf16 cast and slot (or in-place) store
+// -- one streaming pass over the shard.
 //
 // Page "Infra: Data Parallel" (pufanyi.com), section "Zero Redundancy
 // Optimizer (ZeRO)": AdamW is element-wise, so a rank holding a slice of the
 // parameters, the averaged gradient of that slice (Reduce-Scatter with
 // averaging) and the slice's moments updates it alone, then All-Gathers the
-// updated parameters (ZeRO-1/2) or keeps them sharded (ZeRO-3).  Knowledge
-// card "FSDP" (kongchang.com), Core Facts: the float accumulation order of a
-// reduction depends on the parallel configuration, so it is fixed here to
-// ascending rank order.
+// updated parameters (ZeRO-1/2) or keeps them sharded (ZeRO-3).  Section
+// "Naive Data Parallelism": with no_sync the micro-batch gradients are summed
+// locally, each scaled by 1/n_micro; the last of these sums can be folded
+// into the step (zero_shard_step_accumulate).  Knowledge card "FSDP"
+// (kongchang.com), Core Facts: the float accumulation order of a reduction
+// depends on the parallel configuration, so it is fixed here to ascending
+// rank order.
 //
-// Design (gfx950): the step is a pure HBM stream, 2*N_d + 26 bytes per shard
-// element with no reuse, so it is written as a grid-stride loop in which each
-// lane moves 8 elements per iteration with 128-bit non-temporal loads and
-// stores (one 16-byte load per rank, two per fp32 state array).  No LDS, no
-// atomics, no MFMA: every output element belongs to exactly one lane, which
-// makes the result independent of the launch shape.  Each rank count that
-// matters gets its own unrolled instantiation; for large N_d the rank loads
-// are issued in groups so that registers stay within budget while enough
-// bytes are in flight.
+// Design (gfx950): the step is a pure HBM stream (2*N_d + 26 bytes per shard
+// element for bf16 contributions) with no reuse, so it is written as a
+// grid-stride loop in which each lane moves 8 elements per iteration with
+// 128-bit loads and stores (one 16-byte load per rank, two per fp32 state
+// array); the cache hint (non-temporal or not) and the blocks per CU follow
+// the measured read/write mix.  No LDS, no atomics, no MFMA: every output
+// element belongs to exactly one lane, which makes the result independent of
+// the launch shape.  Each rank count that matters gets its own unrolled
+// instantiation; for large N_d the rank loads are issued in groups so that
+// registers stay within budget while enough bytes are in flight.
 #include <cmath>
 #include <cstdint>
 #include <vector>
@@ -45,12 +49,25 @@ struct Region {
   int64_t i0, n0, n, seg, pstride, flat0, flat1;
 };
 
-// Contribution element type: GT_BF16 (2-byte patterns) or GT_F32.
-enum : int { GT_BF16 = 0, GT_F32 = 1 };
+// What a rank hands to the reduction:
+//   GT_BF16      bf16 contributions (2 bytes per element and rank)
+//   GT_F32       binary32 contributions (4)
+//   GT_ACC_BF16  the last no_sync micro-batch folded in: the rank's fp32
+//                accumulator plus its scaled bf16 micro-batch gradient,
+//                rounded to bf16 as the rank would send it (6)
+//   GT_ACC_F32   the same sum kept in binary32 (6)
+enum : int { GT_BF16 = 0, GT_F32 = 1, GT_ACC_BF16 = 2, GT_ACC_F32 = 3 };
+constexpr bool fused(int gt) { return gt >= GT_ACC_BF16; }
+constexpr int contrib_bytes(int gt) { return gt == GT_BF16 ? 2 : (gt == GT_F32 ? 4 : 6); }
 
-template <int NP>
+// Largest rank count of the runtime-N_d instantiation: the pointer arrays
+// travel as kernel arguments.
+constexpr int kMaxNdFused = ZERO_MAX_ND_FUSED;
+
+template <int NP, bool FUSED>
 struct StepArgs {
-  const void* g[NP];
+  const void* g[NP];              // contributions, or (fused) micro-batch gradients
+  const float* a[FUSED ? NP : 1];  // fused: the ranks' fp32 accumulators
   float* master;
   float* m;
   float* v;
@@ -58,15 +75,19 @@ struct StepArgs {
   float* gout;
   Scalars k;
   Region reg;
-  float nd_f, inv_nd;
+  float nd_f, inv_nd, acc_scale;
   int32_t nd, pow2, flat_grad, slot_out;
 };
+
+template <int ND, int GT>
+using ArgsFor =
+    StepArgs<(ND > 0 ? ND : (fused(GT) ? kMaxNdFused : ZERO_MAX_ND)), fused(GT)>;
 
 // Division by N_d; for a power of two the product with the exact reciprocal
 // is the same correctly rounded value (x/2^k and x*2^-k are the same real).
 // POW2 > 0: N_d is known at compile time to be a power of two.
-template <int POW2, int NP>
-__device__ __forceinline__ float average(float a, const StepArgs<NP>& A) {
+template <int POW2, class Args>
+__device__ __forceinline__ float average(float a, const Args& A) {
   if constexpr (POW2 > 0)
     return a * A.inv_nd;
   else
@@ -85,7 +106,10 @@ __device__ __forceinline__ void adamw(float g, float& th, float& m, float& v, co
 
 // 8 consecutive contributions of one rank, as loaded (not yet widened).
 template <int GT>
-struct Raw8;
+struct Raw8 {
+  f32x4 lo, hi;  // fused: the accumulator
+  u32x4 w;       // fused: the micro-batch gradient
+};
 template <>
 struct Raw8<GT_BF16> {
   u32x4 w;
@@ -95,70 +119,107 @@ struct Raw8<GT_F32> {
   f32x4 lo, hi;
 };
 
-template <int GT, bool NT>
-__device__ __forceinline__ Raw8<GT> load8(const void* base, int64_t gi) {
+template <int GT, bool NT, class Args>
+__device__ __forceinline__ Raw8<GT> load8(const Args& A, int q, int64_t gi) {
   Raw8<GT> r;
   if constexpr (GT == GT_BF16) {
-    r.w = ld_stream<NT>((const u32x4*)((const uint16_t*)base + gi));
+    r.w = ld_stream<NT>((const u32x4*)((const uint16_t*)A.g[q] + gi));
+  } else if constexpr (GT == GT_F32) {
+    r.lo = ld_stream<NT>((const f32x4*)((const float*)A.g[q] + gi));
+    r.hi = ld_stream<NT>((const f32x4*)((const float*)A.g[q] + gi + 4));
   } else {
-    r.lo = ld_stream<NT>((const f32x4*)((const float*)base + gi));
-    r.hi = ld_stream<NT>((const f32x4*)((const float*)base + gi + 4));
+    r.lo = ld_stream<NT>((const f32x4*)(A.a[q] + gi));
+    r.hi = ld_stream<NT>((const f32x4*)(A.a[q] + gi + 4));
+    r.w = ld_stream<NT>((const u32x4*)((const uint16_t*)A.g[q] + gi));
   }
   return r;
 }
 
+// A fused contribution: acc + scale*g (product and sum rounded once each, the
+// no_sync accumulation's add), then for GT_ACC_BF16 the bf16 rounding.
 template <int GT>
-__device__ __forceinline__ void widen8(float a[8], const Raw8<GT>& r) {
+__device__ __forceinline__ float fold(float acc, float g, float scale) {
+  const float c = acc + scale * g;
+  if constexpr (GT == GT_ACC_BF16)
+    return __uint_as_float(bf16_round(c) << 16);
+  else
+    return c;
+}
+
+template <int GT, class Args>
+__device__ __forceinline__ void widen8(float x[8], const Raw8<GT>& r, const Args& A) {
   if constexpr (GT == GT_BF16) {
-    a[0] = bf16_lo(r.w.x); a[1] = bf16_hi(r.w.x);
-    a[2] = bf16_lo(r.w.y); a[3] = bf16_hi(r.w.y);
-    a[4] = bf16_lo(r.w.z); a[5] = bf16_hi(r.w.z);
-    a[6] = bf16_lo(r.w.w); a[7] = bf16_hi(r.w.w);
+    x[0] = bf16_lo(r.w.x); x[1] = bf16_hi(r.w.x);
+    x[2] = bf16_lo(r.w.y); x[3] = bf16_hi(r.w.y);
+    x[4] = bf16_lo(r.w.z); x[5] = bf16_hi(r.w.z);
+    x[6] = bf16_lo(r.w.w); x[7] = bf16_hi(r.w.w);
+  } else if constexpr (GT == GT_F32) {
+    x[0] = r.lo.x; x[1] = r.lo.y; x[2] = r.lo.z; x[3] = r.lo.w;
+    x[4] = r.hi.x; x[5] = r.hi.y; x[6] = r.hi.z; x[7] = r.hi.w;
   } else {
-    a[0] = r.lo.x; a[1] = r.lo.y; a[2] = r.lo.z; a[3] = r.lo.w;
-    a[4] = r.hi.x; a[5] = r.hi.y; a[6] = r.hi.z; a[7] = r.hi.w;
+    const float s = A.acc_scale;
+    x[0] = fold<GT>(r.lo.x, bf16_lo(r.w.x), s); x[1] = fold<GT>(r.lo.y, bf16_hi(r.w.x), s);
+    x[2] = fold<GT>(r.lo.z, bf16_lo(r.w.y), s); x[3] = fold<GT>(r.lo.w, bf16_hi(r.w.y), s);
+    x[4] = fold<GT>(r.hi.x, bf16_lo(r.w.z), s); x[5] = fold<GT>(r.hi.y, bf16_hi(r.w.z), s);
+    x[6] = fold<GT>(r.hi.z, bf16_lo(r.w.w), s); x[7] = fold<GT>(r.hi.w, bf16_hi(r.w.w), s);
   }
 }
 
-template <int GT>
-__device__ __forceinline__ void add8(float a[8], const Raw8<GT>& r) {
+template <int GT, class Args>
+__device__ __forceinline__ void add8(float acc[8], const Raw8<GT>& r, const Args& A) {
   float x[8];
-  widen8<GT>(x, r);
+  widen8<GT>(x, r, A);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) a[k] = a[k] + x[k];
+  for (int k = 0; k < 8; ++k) acc[k] = acc[k] + x[k];
 }
 
-template <int GT>
-__device__ __forceinline__ float load_one(const void* base, int64_t gi) {
+template <int GT, class Args>
+__device__ __forceinline__ float load_one(const Args& A, int q, int64_t gi) {
   if constexpr (GT == GT_BF16)
-    return bf16_one(((const uint16_t*)base)[gi]);
+    return bf16_one(((const uint16_t*)A.g[q])[gi]);
+  else if constexpr (GT == GT_F32)
+    return ((const float*)A.g[q])[gi];
   else
-    return ((const float*)base)[gi];
+    return fold<GT>(A.a[q][gi], bf16_one(((const uint16_t*)A.g[q])[gi]), A.acc_scale);
 }
 
 // Sum of the N_d contributions of 8 consecutive elements, ascending rank.
 // The loads of up to GROUP ranks are issued before their adds.
+// The fused contributions at large N_d keep the group loop rolled: fully
+// unrolled, the scheduler hoists loads of later groups and spills.
 template <int ND, int GROUP, bool NT, int GT>
-__device__ __forceinline__ void reduce8(float acc[8], const StepArgs<ND>& A, int64_t gi) {
-  widen8<GT>(acc, load8<GT, NT>(A.g[0], gi));
+__device__ __forceinline__ void reduce8(float acc[8], const ArgsFor<ND, GT>& A, int64_t gi) {
+  widen8<GT>(acc, load8<GT, NT>(A, 0, gi), A);
+  if constexpr (fused(GT) && ND > 16) {
+#pragma unroll 1
+    for (int q0 = 1; q0 < ND; q0 += GROUP) {
+      Raw8<GT> w[GROUP];
+#pragma unroll
+      for (int u = 0; u < GROUP; ++u)
+        if (q0 + u < ND) w[u] = load8<GT, NT>(A, q0 + u, gi);
+#pragma unroll
+      for (int u = 0; u < GROUP; ++u)
+        if (q0 + u < ND) add8<GT>(acc, w[u], A);
+    }
+    return;
+  }
 #pragma unroll
   for (int q0 = 1; q0 < ND; q0 += GROUP) {
     Raw8<GT> w[GROUP];
 #pragma unroll
     for (int u = 0; u < GROUP; ++u)
-      if (q0 + u < ND) w[u] = load8<GT, NT>(A.g[q0 + u], gi);
+      if (q0 + u < ND) w[u] = load8<GT, NT>(A, q0 + u, gi);
 #pragma unroll
     for (int u = 0; u < GROUP; ++u)
-      if (q0 + u < ND) add8<GT>(acc, w[u]);
+      if (q0 + u < ND) add8<GT>(acc, w[u], A);
   }
 }
 
-// Runtime rank count (any N_d up to ZERO_MAX_ND).
+// Runtime rank count.
 template <bool NT, int GT>
-__device__ __forceinline__ void reduce8_dyn(float acc[8], const StepArgs<ZERO_MAX_ND>& A,
-                                            int64_t gi) {
-  widen8<GT>(acc, load8<GT, NT>(A.g[0], gi));
-  for (int q = 1; q < A.nd; ++q) add8<GT>(acc, load8<GT, NT>(A.g[q], gi));
+__device__ __forceinline__ void reduce8_dyn(float acc[8], const ArgsFor<0, GT>& A, int64_t gi) {
+  widen8<GT>(acc, load8<GT, NT>(A, 0, gi), A);
+  for (int q = 1; q < A.nd; ++q) add8<GT>(acc, load8<GT, NT>(A, q, gi), A);
 }
 
 __device__ __forceinline__ int64_t flat_of(const Region& r, int64_t e) {
@@ -167,15 +228,11 @@ __device__ __forceinline__ int64_t flat_of(const Region& r, int64_t e) {
   return r.flat0 + b * r.pstride + (e - b * r.seg);
 }
 
-// One element with generic addressing (tails, the scalar path).
-template <int GT, int NP>
-__device__ __forceinline__ void step_one(const StepArgs<NP>& A, int64_t e, bool map) {
-  const int64_t i = A.reg.i0 + e;
-  const int64_t f = map ? flat_of(A.reg, e) : i;
-  const int64_t gi = (map && A.flat_grad) ? f : i;
-  const int64_t oi = (map && A.slot_out) ? f : i;
-  float a = load_one<GT>(A.g[0], gi);
-  for (int q = 1; q < A.nd; ++q) a = a + load_one<GT>(A.g[q], gi);
+// One element: shard index i, contribution index gi, output index oi.
+template <int GT, class Args>
+__device__ __forceinline__ void step_at(const Args& A, int64_t i, int64_t gi, int64_t oi) {
+  float a = load_one<GT>(A, 0, gi);
+  for (int q = 1; q < A.nd; ++q) a = a + load_one<GT>(A, q, gi);
   const float g = average<0>(a, A);
   float th = A.master[i], m = A.m[i], v = A.v[i];
   adamw(g, th, m, v, A.k);
@@ -186,16 +243,62 @@ __device__ __forceinline__ void step_one(const StepArgs<NP>& A, int64_t e, bool 
   if (A.gout) A.gout[i] = g;
 }
 
-// Vector path: 8 elements per lane per iteration, grid-stride over the
-// launch.  Requires 16-byte aligned bases and i0 % 8 == 0; when mapping,
+// Element e of the launch's Region, generic addressing (tails, scalar path).
+template <int GT, class Args>
+__device__ __forceinline__ void step_one(const Args& A, int64_t e, bool map) {
+  const int64_t i = A.reg.i0 + e;
+  const int64_t f = map ? flat_of(A.reg, e) : i;
+  step_at<GT>(A, i, (map && A.flat_grad) ? f : i, (map && A.slot_out) ? f : i);
+}
+
+// 8 consecutive elements with 128-bit accesses: shard index i, contribution
+// index gi, output index oi (all multiples of 8 on 16-byte aligned bases).
+template <int ND, int GROUP, bool NT, int GT>
+__device__ __forceinline__ void step8(const ArgsFor<ND, GT>& A, int64_t i, int64_t gi,
+                                      int64_t oi) {
+  float acc[8];
+  if constexpr (ND > 0)
+    reduce8<ND, GROUP, NT, GT>(acc, A, gi);
+  else
+    reduce8_dyn<NT, GT>(acc, A, gi);
+
+  const f32x4 th0 = ld_stream<NT>((const f32x4*)(A.master + i));
+  const f32x4 th1 = ld_stream<NT>((const f32x4*)(A.master + i + 4));
+  const f32x4 m0 = ld_stream<NT>((const f32x4*)(A.m + i));
+  const f32x4 m1 = ld_stream<NT>((const f32x4*)(A.m + i + 4));
+  const f32x4 v0 = ld_stream<NT>((const f32x4*)(A.v + i));
+  const f32x4 v1 = ld_stream<NT>((const f32x4*)(A.v + i + 4));
+  float th[8] = {th0.x, th0.y, th0.z, th0.w, th1.x, th1.y, th1.z, th1.w};
+  float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+  float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  float g[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    g[k] = average<((ND & (ND - 1)) == 0 ? ND : 0)>(acc[k], A);
+    adamw(g[k], th[k], mm[k], vv[k], A.k);
+  }
+  st_stream<NT>((f32x4*)(A.master + i), f32x4{th[0], th[1], th[2], th[3]});
+  st_stream<NT>((f32x4*)(A.master + i + 4), f32x4{th[4], th[5], th[6], th[7]});
+  st_stream<NT>((f32x4*)(A.m + i), f32x4{mm[0], mm[1], mm[2], mm[3]});
+  st_stream<NT>((f32x4*)(A.m + i + 4), f32x4{mm[4], mm[5], mm[6], mm[7]});
+  st_stream<NT>((f32x4*)(A.v + i), f32x4{vv[0], vv[1], vv[2], vv[3]});
+  st_stream<NT>((f32x4*)(A.v + i + 4), f32x4{vv[4], vv[5], vv[6], vv[7]});
+  st_stream<NT>((u32x4*)(A.pout + oi),
+                u32x4{bf16_pack2(th[0], th[1]), bf16_pack2(th[2], th[3]),
+                      bf16_pack2(th[4], th[5]), bf16_pack2(th[6], th[7])});
+  if (A.gout) {
+    st_stream<NT>((f32x4*)(A.gout + i), f32x4{g[0], g[1], g[2], g[3]});
+    st_stream<NT>((f32x4*)(A.gout + i + 4), f32x4{g[4], g[5], g[6], g[7]});
+  }
+}
+
+// Vector path over one Region: 8 elements per lane per iteration,
+// grid-stride.  Requires 16-byte aligned bases and i0 % 8 == 0; when mapping,
 // flat0 % 8 == 0 and (part 0 is one bucket, or seg % 8 == 0 and
 // pstride % 8 == 0), and if part 1 exists n0 % 8 == 0 and flat1 % 8 == 0, so
 // that no vector straddles a bucket and every vector address is aligned.
-template <int ND>
-using ArgsFor = StepArgs<(ND > 0 ? ND : ZERO_MAX_ND)>;
-
 template <int ND, bool MAP, int GROUP, bool NT, int GT>
-__global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND> A) {
+__global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND, GT> A) {
   const int64_t n = A.reg.n;
   const int64_t nv0 = A.reg.n0 >> 3;
   const int64_t nvec = (A.reg.n0 == n) ? nv0 : nv0 + ((n - A.reg.n0) >> 3);
@@ -223,51 +326,56 @@ __global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND> A) {
         f = A.reg.flat1 + ((vi - nv0) << 3);
       }
     }
-    const int64_t gi = (MAP && A.flat_grad) ? f : i;
-    const int64_t oi = (MAP && A.slot_out) ? f : i;
-
-    float acc[8];
-    if constexpr (ND > 0)
-      reduce8<ND, GROUP, NT, GT>(acc, A, gi);
-    else
-      reduce8_dyn<NT, GT>(acc, A, gi);
-
-    const f32x4 th0 = ld_stream<NT>((const f32x4*)(A.master + i));
-    const f32x4 th1 = ld_stream<NT>((const f32x4*)(A.master + i + 4));
-    const f32x4 m0 = ld_stream<NT>((const f32x4*)(A.m + i));
-    const f32x4 m1 = ld_stream<NT>((const f32x4*)(A.m + i + 4));
-    const f32x4 v0 = ld_stream<NT>((const f32x4*)(A.v + i));
-    const f32x4 v1 = ld_stream<NT>((const f32x4*)(A.v + i + 4));
-    float th[8] = {th0.x, th0.y, th0.z, th0.w, th1.x, th1.y, th1.z, th1.w};
-    float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-    float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    float g[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      g[k] = average<((ND & (ND - 1)) == 0 ? ND : 0)>(acc[k], A);
-      adamw(g[k], th[k], mm[k], vv[k], A.k);
-    }
-    st_stream<NT>((f32x4*)(A.master + i), f32x4{th[0], th[1], th[2], th[3]});
-    st_stream<NT>((f32x4*)(A.master + i + 4), f32x4{th[4], th[5], th[6], th[7]});
-    st_stream<NT>((f32x4*)(A.m + i), f32x4{mm[0], mm[1], mm[2], mm[3]});
-    st_stream<NT>((f32x4*)(A.m + i + 4), f32x4{mm[4], mm[5], mm[6], mm[7]});
-    st_stream<NT>((f32x4*)(A.v + i), f32x4{vv[0], vv[1], vv[2], vv[3]});
-    st_stream<NT>((f32x4*)(A.v + i + 4), f32x4{vv[4], vv[5], vv[6], vv[7]});
-    st_stream<NT>((u32x4*)(A.pout + oi),
-              u32x4{bf16_pack2(th[0], th[1]), bf16_pack2(th[2], th[3]), bf16_pack2(th[4], th[5]),
-                    bf16_pack2(th[6], th[7])});
-    if (A.gout) {
-      st_stream<NT>((f32x4*)(A.gout + i), f32x4{g[0], g[1], g[2], g[3]});
-      st_stream<NT>((f32x4*)(A.gout + i + 4), f32x4{g[4], g[5], g[6], g[7]});
-    }
+    step8<ND, GROUP, NT, GT>(A, i, (MAP && A.flat_grad) ? f : i, (MAP && A.slot_out) ? f : i);
   }
   // the elements after the last full vector, one per lane
   const int64_t tail0 = (nvec == nv0) ? (nv0 << 3) : A.reg.n0 + ((nvec - nv0) << 3);
   if (tid < n - tail0) step_one<GT>(A, tail0 + tid, MAP);
 }
 
+// Many single-bucket regions in one launch (the per-parameter layout, where
+// every tensor is its own bucket): region k covers shard [i0[k], i0[k]+n[k])
+// and flat [f0[k], f0[k]+n[k]).  The work is cut into tiles of blockDim.x*8
+// elements; blocks take tiles grid-stride and find a tile's region by binary
+// search over the tile prefix sums, so a 38.6M-element embedding and
+// 96-element norm slices share one launch without idle blocks.  Regions whose
+// addresses are not all 16-byte aligned (bit clear in `vec`) run element by
+// element.
+constexpr int kTableMax = 32;
+struct Table {
+  int64_t i0[kTableMax], f0[kTableMax], n[kTableMax];
+  int64_t tile0[kTableMax + 1];  // first tile of each region; tile0[count] = total
+  uint32_t vec;
+  int32_t count;
+};
+
+template <int ND, int GROUP, bool NT, int GT>
+__global__ void __launch_bounds__(256) step_table_kernel(const ArgsFor<ND, GT> A, const Table T) {
+  const int64_t span = (int64_t)blockDim.x << 3;
+  const int64_t total = T.tile0[T.count];
+  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    int lo = 0, hi = T.count;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (T.tile0[mid] <= tile) lo = mid;
+      else hi = mid;
+    }
+    const int64_t n = T.n[lo];
+    const int64_t e0 = (tile - T.tile0[lo]) * span + ((int64_t)threadIdx.x << 3);
+    if (e0 >= n) continue;
+    const int64_t i = T.i0[lo] + e0, f = T.f0[lo] + e0;
+    const int64_t gi = A.flat_grad ? f : i, oi = A.slot_out ? f : i;
+    if (((T.vec >> lo) & 1u) && e0 + 8 <= n) {
+      step8<ND, GROUP, NT, GT>(A, i, gi, oi);
+    } else {
+      const int64_t m = n - e0 < 8 ? n - e0 : 8;
+      for (int64_t e = 0; e < m; ++e) step_at<GT>(A, i + e, gi + e, oi + e);
+    }
+  }
+}
+
 template <int GT>
-__global__ void __launch_bounds__(256) step_scalar_kernel(const StepArgs<ZERO_MAX_ND> A, int map) {
+__global__ void __launch_bounds__(256) step_scalar_kernel(const ArgsFor<0, GT> A, int map) {
   const int64_t n = A.reg.n;
   const int64_t T = (int64_t)gridDim.x * blockDim.x;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += T)
@@ -277,16 +385,21 @@ __global__ void __launch_bounds__(256) step_scalar_kernel(const StepArgs<ZERO_MA
 // ------------------------------------------------------------------ host
 struct Call {
   const void* const* g;
+  const float* const* a;  // fused only
   int32_t nd, gt;
+  float acc_scale;
   float *master, *m, *v, *gout;
   uint16_t* pout;
   Scalars k;
   int32_t flat_grad, slot_out;
 };
 
-template <int NP>
-void fill_args(StepArgs<NP>& A, const Call& c, const Region& reg) {
+template <class Args>
+void fill_args(Args& A, const Call& c, const Region& reg) {
+  constexpr int NP = sizeof(A.g) / sizeof(A.g[0]);
+  constexpr int NA = sizeof(A.a) / sizeof(A.a[0]);
   for (int q = 0; q < NP; ++q) A.g[q] = (q < c.nd) ? c.g[q] : nullptr;
+  for (int q = 0; q < NA; ++q) A.a[q] = (c.a && q < c.nd) ? c.a[q] : nullptr;
   A.master = c.master;
   A.m = c.m;
   A.v = c.v;
@@ -298,6 +411,7 @@ void fill_args(StepArgs<NP>& A, const Call& c, const Region& reg) {
   A.nd_f = (float)c.nd;
   A.pow2 = (c.nd & (c.nd - 1)) == 0;
   A.inv_nd = 1.0f / (float)c.nd;
+  A.acc_scale = c.acc_scale;
   A.flat_grad = c.flat_grad;
   A.slot_out = c.slot_out;
 }
@@ -316,63 +430,95 @@ int cu_count() {
 
 constexpr int kDefaultThreads = 256;
 
-// Launch policy, from measurements on MI355X: the read-dominated step
-// (64 or more bytes of contributions per element) streams best with
-// non-temporal accesses and one 256-thread block per CU; the step with a
-// larger write share (small N_d) with ordinary accesses and two blocks per CU.
-constexpr bool read_dominated(int nd, int gt) { return nd * (gt == GT_F32 ? 4 : 2) >= 64; }
-int default_blocks_per_cu(int nd, int gt) { return read_dominated(nd, gt) ? 1 : 2; }
-
-template <int ND, bool MAP, int GT>
-int launch_vec(const Call& c, const Region& reg, int blocks, int threads, hipStream_t s) {
-  StepArgs<ND> A;
-  fill_args(A, c, reg);
-  constexpr int GROUP = (ND > 16) ? 16 : (ND > 1 ? ND - 1 : 1);
-  hipLaunchKernelGGL((step_vec_kernel<ND, MAP, GROUP, read_dominated(ND, GT), GT>), dim3(blocks),
-                     dim3(threads), 0, s, A);
-  return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
-}
-
-template <bool MAP, int GT>
-int dispatch_vec_gt(const Call& c, const Region& reg, int blocks, int threads, hipStream_t s) {
-  switch (c.nd) {
-    case 2: return launch_vec<2, MAP, GT>(c, reg, blocks, threads, s);
-    case 4: return launch_vec<4, MAP, GT>(c, reg, blocks, threads, s);
-    case 8: return launch_vec<8, MAP, GT>(c, reg, blocks, threads, s);
-    case 16: return launch_vec<16, MAP, GT>(c, reg, blocks, threads, s);
-    case 32: return launch_vec<32, MAP, GT>(c, reg, blocks, threads, s);
-    case 64: return launch_vec<64, MAP, GT>(c, reg, blocks, threads, s);
-    default: {
-      StepArgs<ZERO_MAX_ND> A;
-      fill_args(A, c, reg);
-      if (read_dominated(c.nd, GT))
-        hipLaunchKernelGGL((step_vec_kernel<0, MAP, 1, true, GT>), dim3(blocks), dim3(threads), 0,
-                           s, A);
-      else
-        hipLaunchKernelGGL((step_vec_kernel<0, MAP, 1, false, GT>), dim3(blocks), dim3(threads), 0,
-                           s, A);
-      return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
-    }
+// Launch policy, from measurements on MI355X: a read-dominated step (64 or
+// more bytes of contributions per element) streams best with non-temporal
+// accesses and one 256-thread block per CU; a step with a larger write share
+// (small N_d) with ordinary accesses and two blocks per CU.
+constexpr bool read_dominated(int nd, int gt) { return nd * contrib_bytes(gt) >= 64; }
+int default_blocks_per_cu(int nd, int gt) {
+  switch (gt) {
+    case GT_F32: return read_dominated(nd, GT_F32) ? 1 : 2;
+    case GT_ACC_BF16:
+    case GT_ACC_F32: return read_dominated(nd, GT_ACC_BF16) ? 1 : 2;
+    default: return read_dominated(nd, GT_BF16) ? 1 : 2;
   }
 }
 
-template <bool MAP>
-int dispatch_vec(const Call& c, const Region& reg, int blocks, int threads, hipStream_t s) {
-  return c.gt == GT_F32 ? dispatch_vec_gt<MAP, GT_F32>(c, reg, blocks, threads, s)
-                        : dispatch_vec_gt<MAP, GT_BF16>(c, reg, blocks, threads, s);
+// What one launch covers: a Region (affine addressing, with or without the
+// flat map) or a Table of single-bucket regions.
+enum : int { K_PLAIN = 0, K_MAP = 1, K_TABLE = 2 };
+struct Work {
+  const Region* reg;
+  const Table* tab;
+  int blocks, threads;
+};
+
+template <int ND, int GT, int KIND, bool NT>
+int launch_nt(const Call& c, const Work& w, hipStream_t s) {
+  ArgsFor<ND, GT> A;
+  fill_args(A, c, w.reg ? *w.reg : Region{0, 0, 0, 1, 0, 0, 0});
+  // ranks whose loads are in flight together: 16 (8 for the 12-dword fused
+  // loads, which would otherwise spill at N_d = 64)
+  constexpr int GMAX = fused(GT) ? 8 : 16;
+  constexpr int GROUP = ND > GMAX ? GMAX : (ND > 1 ? ND - 1 : 1);
+  if constexpr (KIND == K_TABLE)
+    hipLaunchKernelGGL((step_table_kernel<ND, GROUP, NT, GT>), dim3(w.blocks), dim3(w.threads), 0,
+                       s, A, *w.tab);
+  else
+    hipLaunchKernelGGL((step_vec_kernel<ND, KIND == K_MAP, GROUP, NT, GT>), dim3(w.blocks),
+                       dim3(w.threads), 0, s, A);
+  return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
+}
+
+template <int ND, int GT, int KIND>
+int launch(const Call& c, const Work& w, hipStream_t s) {
+  if constexpr (ND > 0)
+    return launch_nt<ND, GT, KIND, read_dominated(ND, GT)>(c, w, s);
+  else
+    return read_dominated(c.nd, GT) ? launch_nt<0, GT, KIND, true>(c, w, s)
+                                    : launch_nt<0, GT, KIND, false>(c, w, s);
+}
+
+template <int GT, int KIND>
+int dispatch_nd(const Call& c, const Work& w, hipStream_t s) {
+  switch (c.nd) {
+    case 2: return launch<2, GT, KIND>(c, w, s);
+    case 4: return launch<4, GT, KIND>(c, w, s);
+    case 8: return launch<8, GT, KIND>(c, w, s);
+    case 16: return launch<16, GT, KIND>(c, w, s);
+    case 32: return launch<32, GT, KIND>(c, w, s);
+    case 64: return launch<64, GT, KIND>(c, w, s);
+    default: return launch<0, GT, KIND>(c, w, s);
+  }
+}
+
+template <int KIND>
+int dispatch(const Call& c, const Work& w, hipStream_t s) {
+  switch (c.gt) {
+    case GT_F32: return dispatch_nd<GT_F32, KIND>(c, w, s);
+    case GT_ACC_BF16: return dispatch_nd<GT_ACC_BF16, KIND>(c, w, s);
+    case GT_ACC_F32: return dispatch_nd<GT_ACC_F32, KIND>(c, w, s);
+    default: return dispatch_nd<GT_BF16, KIND>(c, w, s);
+  }
+}
+
+template <int GT>
+int launch_scalar_gt(const Call& c, const Region& reg, bool map, int blocks, int threads,
+                     hipStream_t s) {
+  ArgsFor<0, GT> A;
+  fill_args(A, c, reg);
+  hipLaunchKernelGGL(step_scalar_kernel<GT>, dim3(blocks), dim3(threads), 0, s, A, map ? 1 : 0);
+  return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
 }
 
 int launch_scalar(const Call& c, const Region& reg, bool map, int blocks, int threads,
                   hipStream_t s) {
-  StepArgs<ZERO_MAX_ND> A;
-  fill_args(A, c, reg);
-  if (c.gt == GT_F32)
-    hipLaunchKernelGGL(step_scalar_kernel<GT_F32>, dim3(blocks), dim3(threads), 0, s, A,
-                       map ? 1 : 0);
-  else
-    hipLaunchKernelGGL(step_scalar_kernel<GT_BF16>, dim3(blocks), dim3(threads), 0, s, A,
-                       map ? 1 : 0);
-  return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
+  switch (c.gt) {
+    case GT_F32: return launch_scalar_gt<GT_F32>(c, reg, map, blocks, threads, s);
+    case GT_ACC_BF16: return launch_scalar_gt<GT_ACC_BF16>(c, reg, map, blocks, threads, s);
+    case GT_ACC_F32: return launch_scalar_gt<GT_ACC_F32>(c, reg, map, blocks, threads, s);
+    default: return launch_scalar_gt<GT_BF16>(c, reg, map, blocks, threads, s);
+  }
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -407,93 +553,105 @@ Scalars make_scalars(const zero_adamw& hp, int64_t t) {
   return k;
 }
 
-}  // namespace
+struct LaunchShape {
+  int threads = kDefaultThreads, blocks_cap = 0, path = 0;
+};
 
-extern "C" {
-
-int zero_step_scalars(const zero_adamw* hp, int64_t t, float out[8]) {
-  if (!hp || !out || t < 1 || !hp_ok(*hp)) return ZERO_EINVAL;
-  const Scalars k = make_scalars(*hp, t);
-  out[0] = k.s; out[1] = k.rho; out[2] = k.a_wd; out[3] = k.B1;
-  out[4] = k.C1; out[5] = k.B2; out[6] = k.C2; out[7] = k.E;
+int parse_options(const zero_step_options* opt, LaunchShape& ls) {
+  if (!opt) return ZERO_OK;
+  if (opt->threads > 0) ls.threads = opt->threads;
+  if (opt->blocks > 0) ls.blocks_cap = opt->blocks;
+  ls.path = opt->path;
+  if (ls.threads % 64 != 0 || ls.threads > 256 || (ls.path != 0 && ls.path != 1))
+    return ZERO_EINVAL;
   return ZERO_OK;
 }
 
-int zero_shard_step_ex(const zero_layout* L, const zero_adamw* hp, int64_t t,
-                       const void* const* rank_grads, int32_t grad_layout, float* master,
-                       float* exp_avg, float* exp_avg_sq, uint16_t* param_out, int32_t out_mode,
-                       float* reduced_grad_out, const zero_step_options* opt,
-                       hipStream_t stream) {
-  if (!L || !hp || !rank_grads || t < 1 || !hp_ok(*hp)) return ZERO_EINVAL;
+// Validates everything common to the step entry points, plans the launches
+// and enqueues them.  `ins`/`in_bytes`: the contribution buffers of every
+// rank (two per rank when fused), each of in_bytes bytes.
+int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int32_t grad_layout,
+             int32_t out_mode, const LaunchShape& ls, const void* const* ins, int n_ins,
+             const int64_t* in_bytes, hipStream_t stream) {
   if (grad_layout != ZERO_GRAD_COMPACT && grad_layout != ZERO_GRAD_FLAT) return ZERO_EINVAL;
   if (out_mode != ZERO_OUT_AG_SLOT && out_mode != ZERO_OUT_SHARD) return ZERO_EINVAL;
-  int threads = kDefaultThreads, blocks_cap = 0, path = 0, gt = GT_BF16;
-  if (opt) {
-    if (opt->grad_dtype != ZERO_DTYPE_BF16 && opt->grad_dtype != ZERO_DTYPE_F32)
-      return ZERO_EINVAL;
-    gt = opt->grad_dtype == ZERO_DTYPE_F32 ? GT_F32 : GT_BF16;
-    if (opt->threads > 0) threads = opt->threads;
-    if (opt->blocks > 0) blocks_cap = opt->blocks;
-    path = opt->path;
-    if (threads % 64 != 0 || threads > 256 || (path != 0 && path != 1)) return ZERO_EINVAL;
-  }
   const int32_t nd = L->n_d;
   const int64_t S = L->S, P = L->P;
   if (S == 0) return ZERO_OK;
-  if (!master || !exp_avg || !exp_avg_sq || !param_out) return ZERO_EINVAL;
-  for (int32_t q = 0; q < nd; ++q)
-    if (!rank_grads[q]) return ZERO_EINVAL;
+  if (!c.master || !c.m || !c.v || !c.pout) return ZERO_EINVAL;
+  for (int q = 0; q < n_ins; ++q)
+    if (!ins[q]) return ZERO_EINVAL;
 
   // outputs must not overlap each other or any input
-  const int64_t gbytes = (gt == GT_F32 ? 4 : 2) * (grad_layout == ZERO_GRAD_FLAT ? P : S);
-  const Span outs[5] = {span(master, 4 * S), span(exp_avg, 4 * S), span(exp_avg_sq, 4 * S),
-                        span(param_out, 2 * (out_mode == ZERO_OUT_AG_SLOT ? P : S)),
-                        span(reduced_grad_out, reduced_grad_out ? 4 * S : 0)};
+  const Span outs[5] = {span(c.master, 4 * S), span(c.m, 4 * S), span(c.v, 4 * S),
+                        span(c.pout, 2 * (out_mode == ZERO_OUT_AG_SLOT ? P : S)),
+                        span(c.gout, c.gout ? 4 * S : 0)};
   for (int a = 0; a < 5; ++a) {
     for (int b = a + 1; b < 5; ++b)
       if (overlaps(outs[a], outs[b])) return ZERO_EOVERLAP;
-    for (int32_t q = 0; q < nd; ++q)
-      if (overlaps(outs[a], span(rank_grads[q], gbytes))) return ZERO_EOVERLAP;
+    for (int q = 0; q < n_ins; ++q)
+      if (overlaps(outs[a], span(ins[q], in_bytes[q]))) return ZERO_EOVERLAP;
   }
 
-  Call c;
-  c.g = rank_grads;
   c.nd = nd;
-  c.gt = gt;
-  c.master = master;
-  c.m = exp_avg;
-  c.v = exp_avg_sq;
-  c.gout = reduced_grad_out;
-  c.pout = param_out;
   c.k = make_scalars(*hp, t);
   c.flat_grad = grad_layout == ZERO_GRAD_FLAT;
   c.slot_out = out_mode == ZERO_OUT_AG_SLOT;
   const bool map = c.flat_grad || c.slot_out;
 
-  bool aligned = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) &&
-                 aligned16(param_out) && (!reduced_grad_out || aligned16(reduced_grad_out));
-  for (int32_t q = 0; q < nd; ++q) aligned = aligned && aligned16(rank_grads[q]);
-  const int cap = blocks_cap > 0 ? blocks_cap : cu_count() * default_blocks_per_cu(nd, gt);
-  const bool allow_vec = path == 0 && aligned;
+  bool aligned = aligned16(c.master) && aligned16(c.m) && aligned16(c.v) && aligned16(c.pout) &&
+                 (!c.gout || aligned16(c.gout));
+  for (int q = 0; q < n_ins; ++q) aligned = aligned && aligned16(ins[q]);
+  const int threads = ls.threads;
+  const int cap = ls.blocks_cap > 0 ? ls.blocks_cap : cu_count() * default_blocks_per_cu(nd, c.gt);
+  const bool allow_vec = ls.path == 0 && aligned;
+  const int64_t r = L->rank;
 
-  // Launch plan.  Without flat addressing the shard is one plain range.
+  if (map && !L->fixed()) {
+    // per-parameter (dim-0) layout: every tensor is its own bucket; the
+    // non-empty slices go to table launches of up to kTableMax regions
+    const int64_t span_e = (int64_t)threads * 8;
+    Table T;
+    T.count = 0;
+    T.vec = 0;
+    T.tile0[0] = 0;
+    auto flush = [&]() -> int {
+      if (T.count == 0) return ZERO_OK;
+      const int64_t total = T.tile0[T.count];
+      const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(total, cap));
+      const Work w{nullptr, &T, blocks, threads};
+      const int rc = dispatch<K_TABLE>(c, w, stream);
+      T.count = 0;
+      T.vec = 0;
+      return rc;
+    };
+    for (int64_t b = 0; b < L->nb; ++b) {
+      const int64_t sl = L->bucket_slice(b);
+      if (sl == 0) continue;
+      const int64_t i0 = L->bucket_shard_off(b), f0 = L->bucket_padded_off(b) + r * sl;
+      const int k = T.count;
+      T.i0[k] = i0;
+      T.f0[k] = f0;
+      T.n[k] = sl;
+      if (allow_vec && i0 % 8 == 0 && f0 % 8 == 0) T.vec |= 1u << k;
+      T.tile0[k + 1] = T.tile0[k] + (sl + span_e - 1) / span_e;
+      T.count = k + 1;
+      if (T.count == kTableMax) {
+        const int rc = flush();
+        if (rc != ZERO_OK) return rc;
+        T.tile0[0] = 0;
+      }
+    }
+    return flush();
+  }
+
+  // Bucketed layout.  Without flat addressing the shard is one plain range.
   // With it: part 0 = the full buckets, part 1 = the last bucket; one vector
   // launch covers both when every vector address is aligned, otherwise the
   // parts that are not aligned go to the scalar kernel.
   std::vector<Region> regs;
   std::vector<bool> vec;
-  const int64_t r = L->rank;
-  if (map && !L->fixed()) {
-    // per-parameter (dim-0) layout: every tensor is its own bucket; one
-    // single-bucket launch per non-empty slice
-    for (int64_t b = 0; b < L->nb; ++b) {
-      const int64_t sl = L->bucket_slice(b);
-      if (sl == 0) continue;
-      const int64_t i0 = L->bucket_shard_off(b), f0 = L->bucket_padded_off(b) + r * sl;
-      regs.push_back(Region{i0, sl, sl, sl, 0, f0, 0});
-      vec.push_back(allow_vec && i0 % 8 == 0 && f0 % 8 == 0);
-    }
-  } else if (!map) {
+  if (!map) {
     regs.push_back(Region{0, S, S, S, 0, 0, 0});
     vec.push_back(allow_vec);
   } else if (L->nb == 1 || L->s_last == L->s_full) {
@@ -528,8 +686,8 @@ int zero_shard_step_ex(const zero_layout* L, const zero_adamw* hp, int64_t t,
       const int64_t work = std::max<int64_t>(R.n >> 3, 8);
       const int blocks =
           (int)std::max<int64_t>(1, std::min<int64_t>((work + threads - 1) / threads, cap));
-      rc = map ? dispatch_vec<true>(c, R, blocks, threads, stream)
-               : dispatch_vec<false>(c, R, blocks, threads, stream);
+      const Work w{&R, nullptr, blocks, threads};
+      rc = map ? dispatch<K_MAP>(c, w, stream) : dispatch<K_PLAIN>(c, w, stream);
     } else {
       const int blocks =
           (int)std::max<int64_t>(1, std::min<int64_t>((R.n + threads - 1) / threads, cap));
@@ -538,6 +696,84 @@ int zero_shard_step_ex(const zero_layout* L, const zero_adamw* hp, int64_t t,
     if (rc != ZERO_OK) return rc;
   }
   return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int zero_step_scalars(const zero_adamw* hp, int64_t t, float out[8]) {
+  if (!hp || !out || t < 1 || !hp_ok(*hp)) return ZERO_EINVAL;
+  const Scalars k = make_scalars(*hp, t);
+  out[0] = k.s; out[1] = k.rho; out[2] = k.a_wd; out[3] = k.B1;
+  out[4] = k.C1; out[5] = k.B2; out[6] = k.C2; out[7] = k.E;
+  return ZERO_OK;
+}
+
+int zero_shard_step_ex(const zero_layout* L, const zero_adamw* hp, int64_t t,
+                       const void* const* rank_grads, int32_t grad_layout, float* master,
+                       float* exp_avg, float* exp_avg_sq, uint16_t* param_out, int32_t out_mode,
+                       float* reduced_grad_out, const zero_step_options* opt,
+                       hipStream_t stream) {
+  if (!L || !hp || !rank_grads || t < 1 || !hp_ok(*hp)) return ZERO_EINVAL;
+  int gt = GT_BF16;
+  if (opt) {
+    if (opt->grad_dtype != ZERO_DTYPE_BF16 && opt->grad_dtype != ZERO_DTYPE_F32)
+      return ZERO_EINVAL;
+    gt = opt->grad_dtype == ZERO_DTYPE_F32 ? GT_F32 : GT_BF16;
+  }
+  LaunchShape ls;
+  if (parse_options(opt, ls) != ZERO_OK) return ZERO_EINVAL;
+  const int64_t n_in = grad_layout == ZERO_GRAD_FLAT ? L->P : L->S;
+  std::vector<int64_t> bytes((size_t)L->n_d, contrib_bytes(gt) * n_in);
+  Call c{};
+  c.g = rank_grads;
+  c.a = nullptr;
+  c.gt = gt;
+  c.acc_scale = 0.0f;
+  c.master = master;
+  c.m = exp_avg;
+  c.v = exp_avg_sq;
+  c.gout = reduced_grad_out;
+  c.pout = param_out;
+  return run_step(L, hp, t, c, grad_layout, out_mode, ls, rank_grads, L->n_d, bytes.data(),
+                  stream);
+}
+
+int zero_shard_step_accumulate(const zero_layout* L, const zero_adamw* hp, int64_t t,
+                               const float* const* rank_acc, const uint16_t* const* rank_micro,
+                               float micro_scale, int32_t contrib_dtype, int32_t grad_layout,
+                               float* master, float* exp_avg, float* exp_avg_sq,
+                               uint16_t* param_out, int32_t out_mode, float* reduced_grad_out,
+                               const zero_step_options* opt, hipStream_t stream) {
+  if (!L || !hp || !rank_acc || !rank_micro || t < 1 || !hp_ok(*hp)) return ZERO_EINVAL;
+  if (contrib_dtype != ZERO_DTYPE_BF16 && contrib_dtype != ZERO_DTYPE_F32) return ZERO_EINVAL;
+  if (!std::isfinite(micro_scale)) return ZERO_EINVAL;
+  if (L->n_d > ZERO_MAX_ND_FUSED) return ZERO_ERANGE;
+  LaunchShape ls;
+  if (parse_options(opt, ls) != ZERO_OK) return ZERO_EINVAL;
+  const int32_t nd = L->n_d;
+  const int64_t n_in = grad_layout == ZERO_GRAD_FLAT ? L->P : L->S;
+  std::vector<const void*> ins((size_t)2 * nd);
+  std::vector<int64_t> bytes((size_t)2 * nd);
+  for (int32_t q = 0; q < nd; ++q) {
+    ins[2 * q] = rank_acc[q];
+    bytes[2 * q] = 4 * n_in;
+    ins[2 * q + 1] = rank_micro[q];
+    bytes[2 * q + 1] = 2 * n_in;
+  }
+  Call c{};
+  c.g = (const void* const*)rank_micro;
+  c.a = rank_acc;
+  c.gt = contrib_dtype == ZERO_DTYPE_F32 ? GT_ACC_F32 : GT_ACC_BF16;
+  c.acc_scale = micro_scale;
+  c.master = master;
+  c.m = exp_avg;
+  c.v = exp_avg_sq;
+  c.gout = reduced_grad_out;
+  c.pout = param_out;
+  return run_step(L, hp, t, c, grad_layout, out_mode, ls, ins.data(), 2 * nd, bytes.data(),
+                  stream);
 }
 
 int zero_shard_step(const zero_layout* L, const zero_adamw* hp, int64_t t,

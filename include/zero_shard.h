@@ -57,8 +57,10 @@ typedef enum {
   ZERO_EOVERLAP = -5  /* an output buffer overlaps an input or another output */
 } zero_status;
 
-/* Largest number of data-parallel ranks a call accepts. */
+/* Largest number of data-parallel ranks a call accepts
+ * (zero_shard_step_accumulate: ZERO_MAX_ND_FUSED). */
 #define ZERO_MAX_ND 256
+#define ZERO_MAX_ND_FUSED 128
 
 /* ------------------------------------------------------------------ layout
  * Bucketed flat layout ("Naive Data Parallelism": buckets; "FSDP1": flatten,
@@ -245,6 +247,43 @@ int zero_shard_step_ex(const zero_layout* layout, const zero_adamw* hp, int64_t 
                        float* master_dev, float* exp_avg_dev, float* exp_avg_sq_dev,
                        uint16_t* param_out_dev, int32_t out_mode, float* reduced_grad_out_dev,
                        const zero_step_options* opt, hipStream_t stream);
+
+/* The last no_sync micro-batch folded into the step ("Naive Data
+ * Parallelism": micro-batch gradients are accumulated locally, each scaled by
+ * 1/n_micro, and the sum is what a rank contributes to the reduction).
+ *
+ * Rank q's contribution is computed inside the step instead of by a separate
+ * accumulate call:
+ *   c_q = acc_q[i] + micro_scale * bf16->f32(micro_q[i])
+ *   (product and sum rounded once each, as zero_grad_accumulate's add), then
+ *   contrib_dtype ZERO_DTYPE_BF16: G_q = bf16(c_q) (round to nearest even),
+ *     what the rank would hand to a bf16 Reduce-Scatter: the result equals
+ *     zero_grad_accumulate(acc_q, micro_q, n, micro_scale,
+ *     ZERO_ACC_EMIT_BF16 | ZERO_ACC_NO_STORE, tmp_q) for every q followed by
+ *     zero_shard_step on the tmp_q, bit for bit;
+ *   contrib_dtype ZERO_DTYPE_F32: G_q = c_q, equal to accumulating into acc_q
+ *     and calling zero_shard_step_ex with ZERO_DTYPE_F32 on the acc_q.
+ * The reduction and update are those of zero_shard_step.  The accumulators
+ * are read, not written (no_sync restarts them at the next step).  Moves
+ * 6*n_d + 26 bytes per shard element, against 10*n_d + 26 for the separate
+ * accumulate call and step (bf16 contributions).
+ *
+ * rank_acc_dev: HOST array of n_d DEVICE pointers to binary32 accumulators,
+ * rank_micro_dev: HOST array of n_d DEVICE pointers to the bf16 gradients of
+ * the last micro-batch, both in the grad_layout's shape (COMPACT: S values
+ * in shard order; FLAT: whole padded flat buffers of P values).  The other
+ * arguments are those of zero_shard_step_ex; opt->grad_dtype is ignored
+ * (opt may be NULL).  n_d must be at most ZERO_MAX_ND_FUSED (ZERO_ERANGE).
+ * Errors: as for zero_shard_step_ex, plus ZERO_EINVAL for a bad
+ * contrib_dtype or a non-finite micro_scale. */
+int zero_shard_step_accumulate(const zero_layout* layout, const zero_adamw* hp, int64_t t,
+                               const float* const* rank_acc_dev,
+                               const uint16_t* const* rank_micro_dev, float micro_scale,
+                               int32_t contrib_dtype, int32_t grad_layout, float* master_dev,
+                               float* exp_avg_dev, float* exp_avg_sq_dev,
+                               uint16_t* param_out_dev, int32_t out_mode,
+                               float* reduced_grad_out_dev, const zero_step_options* opt,
+                               hipStream_t stream);
 
 /* --------------------------------------------------------- parameter gather
  * ("Zero Redundancy Optimizer (ZeRO)": ZeRO-1/2 All-Gather the updated

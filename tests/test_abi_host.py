@@ -206,6 +206,37 @@ def test_step_argument_errors_before_launch():
     del fake
 
 
+def test_fused_accumulate_step_argument_errors():
+    """zero_shard_step_accumulate validates on the host, like the step."""
+    lib = z.load()
+    E = z.binding
+    L = z.Layout([64], 0, 2, 0)                      # S = 32
+    hp = binding._AdamW(1e-3, 0.9, 0.95, 1e-8, 0.1)
+    acc = (C.c_void_p * 2)(0x100000, 0x110000)
+    mic = (C.c_void_p * 2)(0x200000, 0x210000)
+
+    def call(layout=L.handle, a=acc, g=mic, scale=0.25, dt=0, gl=0, master=0x300000, p=0x600000,
+             om=1, opt=None):
+        return lib.zero_shard_step_accumulate(layout, C.byref(hp), 1, a, g, scale, dt, gl, master,
+                                              0x400000, 0x500000, p, om, None, opt, None)
+
+    assert call(a=None) == E.ZERO_EINVAL
+    assert call(g=None) == E.ZERO_EINVAL
+    assert call(a=(C.c_void_p * 2)(0x100000, None)) == E.ZERO_EINVAL
+    assert call(g=(C.c_void_p * 2)(None, 0x210000)) == E.ZERO_EINVAL
+    assert call(dt=2) == E.ZERO_EINVAL
+    assert call(scale=float("nan")) == E.ZERO_EINVAL
+    assert call(gl=3) == E.ZERO_EINVAL
+    assert call(opt=C.byref(binding._Options(0, 0, 96, 0))) == E.ZERO_EINVAL
+    # 32 fp32 accumulators are 128 bytes: one that ends 64 bytes into master overlaps it
+    assert call(a=(C.c_void_p * 2)(0x300000 - 64, 0x110000)) == E.ZERO_EOVERLAP
+    assert call(p=0x210000 + 8) == E.ZERO_EOVERLAP
+    big = z.Layout([1000], 0, E.ZERO_MAX_ND_FUSED + 1, 0)
+    arr = (C.c_void_p * big.n_d)(*[0x1000000 + 0x10000 * k for k in range(big.n_d)])
+    assert call(layout=big.handle, a=arr, g=arr) == E.ZERO_ERANGE
+    assert call(layout=z.Layout([], 0, 2, 0).handle) == E.ZERO_OK
+
+
 def test_accumulate_and_pack_argument_errors():
     lib = z.load()
     E = z.binding

@@ -546,6 +546,161 @@ def test_no_sync_fp32_accumulators_feed_the_step():
     assert_bitwise(case.master.cpu().numpy(), case.o_master, "master")
 
 
+# ------------------------------------------------------------------ last micro-batch folded in
+def _contribs(case, t, flat, kind, micro, dist, out_type):
+    """Per-rank buffers keyed by (kind, rank, micro, t), COMPACT (S values in
+    shard order) or FLAT (the padded flat buffer, zero padding), with the
+    oracle's values at this rank's shard positions."""
+    w, pl = case.w, case.pl
+    if flat:
+        segs = [(int(po), int(so), int(ln), int(pln - ln))
+                for so, ln, po, pln in zip(pl.stream_off, pl.len, pl.padded_off, pl.padded_len)]
+        n = case.P
+    else:
+        segs, n = case.segs, case.S
+    dtype = torch.float32 if out_type == synth.OUT_F32 else torch.int16
+    dev, host = [], []
+    for q in range(w.n_d):
+        k = synth.key(w.name, kind, q, micro, t)
+        g = torch.empty(n, dtype=dtype, device=DEV)
+        synth.fill_device(g, segs, k, *dist)
+        dev.append(g)
+        host.append(synth.values_at(case.stream_pos, k, *dist, out_type))
+    return dev, host
+
+
+def _fused_oracle(case, t, o_acc, o_micro, scale, contrib):
+    """The separate calls the fused step stands for: each rank's last
+    accumulate (emit bf16 without storing, or store fp32), then the step."""
+    outs = []
+    for a, g in zip(o_acc, o_micro):
+        a = a.copy()
+        if contrib == z.DTYPE_BF16:
+            outs.append(oracle.accumulate(a, g, scale, overwrite=False, store_acc=False,
+                                          emit=True))
+        else:
+            oracle.accumulate(a, g, scale, overwrite=False)
+            outs.append(a)
+    step = oracle.shard_step if contrib == z.DTYPE_BF16 else oracle.shard_step_f32
+    case.o_p, case.o_g = step(outs, case.o_master, case.o_m, case.o_v, case.hp_o, t,
+                              want_grad=True)
+
+
+FUSED_EDGE = [
+    ([1000, 37, 4096, 3], 1500, 4, 3, "flat", "ag_slot"),
+    ([17], 0, 1, 0, "compact", "shard"),
+    ([5, 0, 123, 64], 40, 3, 2, "flat", "ag_slot"),
+    ([70000, 3], 16384, 8, 7, "flat", "ag_slot"),
+    ([50000], 8008, 8, 3, "compact", "ag_slot"),
+    ([20000, 20001], 0, 16, 15, "compact", "shard"),
+    ([64 * 300 + 1], 6400, 64, 63, "compact", "shard"),
+    ([100 * 97], 0, 100, 99, "flat", "ag_slot"),
+    ([128 * 40 + 3], 0, 128, 127, "compact", "ag_slot"),
+]
+
+
+@pytest.mark.parametrize("contrib", [z.DTYPE_BF16, z.DTYPE_F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("numel,cap,n_d,rank,gl,om", FUSED_EDGE)
+def test_fused_last_micro_batch_full_compare(numel, cap, n_d, rank, gl, om, contrib):
+    """zero_shard_step_accumulate against the oracle's last accumulate call
+    followed by its step, every element, three steps."""
+    case = _edge_case(numel, cap, n_d, rank, gl, om)
+    say(f"  fused numel={numel} cap={cap} n_d={n_d} r={rank} {gl} {om} dtype={contrib}: "
+        f"S={case.S}")
+    case.init_state_gpu()
+    case.init_state_oracle()
+    flat = gl == "flat"
+    for t in (1, 2, 3):
+        acc, o_acc = _contribs(case, t, flat, "grad", 0, ("normal", 1e-3), synth.OUT_F32)
+        mic, o_mic = _contribs(case, t, flat, "micro_grad", 3, ("normal", 2e-3), synth.OUT_BF16)
+        z.zero_shard_step_accumulate(
+            case.L, case.hp_z, t, acc, mic, 0.25, contrib,
+            z.GRAD_FLAT if flat else z.GRAD_COMPACT, case.master, case.m, case.v, case.pout,
+            z.OUT_AG_SLOT if om == "ag_slot" else z.OUT_SHARD, case.gout)
+        _fused_oracle(case, t, o_acc, o_mic, 0.25, contrib)
+    torch.cuda.synchronize()
+    case.compare("fused")
+    for a, b in ((case.master, case.o_master), (case.m, case.o_m), (case.v, case.o_v)):
+        assert_bitwise(a.cpu().numpy(), b, "state")
+    pos = case.flat_pos if om == "ag_slot" else np.arange(case.S)
+    assert_bitwise(u16(case.pout)[pos], case.o_p, "param")
+    case.check_canaries(n_probe=4096)
+
+
+@pytest.mark.parametrize("launch", [(3, 64, 0), (0, 0, 1), (5000, 256, 0)])
+def test_fused_launch_shape_invariance(launch):
+    outs = []
+    for lc in (None, launch):
+        case = _edge_case([200_003, 77], 65_536, 16, 9, "flat", "ag_slot")
+        case.init_state_gpu()
+        acc, _ = _contribs(case, 4, True, "grad", 0, ("normal", 1e-3), synth.OUT_F32)
+        mic, _ = _contribs(case, 4, True, "micro_grad", 3, ("normal", 2e-3), synth.OUT_BF16)
+        z.zero_shard_step_accumulate(case.L, case.hp_z, 4, acc, mic, 0.25, z.DTYPE_BF16,
+                                     z.GRAD_FLAT, case.master, case.m, case.v, case.pout,
+                                     z.OUT_AG_SLOT, case.gout, launch=lc)
+        torch.cuda.synchronize()
+        outs.append([case.master.cpu().numpy(), u16(case.pout), case.gout.cpu().numpy()])
+    for a, b in zip(*outs):
+        assert_bitwise(a, b, f"fused launch {launch}")
+
+
+@pytest.mark.timeout(600)
+def test_accum1p3b_fused_sampled():
+    """1.3e9 flat parameters, N_d = 8: every rank accumulates micro-batches
+    1-3 (no_sync, 1/4 each), then the step takes each rank's accumulator and
+    micro-batch 4 directly.  Sampled against the oracle's four accumulate
+    calls and step; at full size every output also equals the separate last
+    accumulate call + step (the same library's other route)."""
+    w = workloads.get("accum1p3b")
+    case = Case(w)
+    case.__init__(w, sample_idx=sample_indices(case.S, case.pl))
+    case.init_state_gpu()
+    case.init_state_oracle()
+    S = case.S
+    accs, lasts, o_accs, o_lasts = [], [], [], []
+    for q in range(w.n_d):
+        say(f"  accumulate rank {q}")
+        acc = torch.empty(S, dtype=torch.float32, device=DEV)
+        micro = torch.empty(S, dtype=torch.int16, device=DEV)
+        o_acc = np.zeros(case.idx.size, np.float32)
+        for k in range(w.n_micro):
+            key = synth.key(w.name, "micro_grad", q, k, w.t_first)
+            synth.fill_device(micro, case.segs, key, *w.micro_grad)
+            o_micro = synth.values_at(case.stream_pos, key, *w.micro_grad, synth.OUT_BF16)
+            if k + 1 < w.n_micro:
+                z.zero_grad_accumulate(acc, micro, 1.0 / w.n_micro,
+                                       z.ACC_OVERWRITE if k == 0 else 0)
+                oracle.accumulate(o_acc, o_micro, 1.0 / w.n_micro, overwrite=(k == 0))
+        accs.append(acc)
+        lasts.append(micro)
+        o_accs.append(o_acc)
+        o_lasts.append(o_micro)
+    say("  fused step t=101")
+    z.zero_shard_step_accumulate(case.L, case.hp_z, w.t_first, accs, lasts, 1.0 / w.n_micro,
+                                 z.DTYPE_BF16, z.GRAD_COMPACT, case.master, case.m, case.v,
+                                 case.pout, z.OUT_AG_SLOT, case.gout)
+    _fused_oracle(case, w.t_first, o_accs, o_lasts, 1.0 / w.n_micro, z.DTYPE_BF16)
+    torch.cuda.synchronize()
+    stats = case.compare("accum1p3b fused")
+    say(f"  accum1p3b fused: exact matches {stats} of {case.idx.size}")
+    case.check_canaries()
+    fused_out = [case.master.cpu(), case.pout.cpu(), case.gout.cpu()]
+    # the separate route on the same inputs, from the same initial state
+    case.init_state_gpu()
+    contribs = []
+    for q in range(w.n_d):
+        c = torch.empty(S, dtype=torch.int16, device=DEV)
+        z.zero_grad_accumulate(accs[q], lasts[q], 1.0 / w.n_micro,
+                               z.ACC_EMIT_BF16 | z.ACC_NO_STORE, c)
+        contribs.append(c)
+    del accs, lasts
+    case.step_gpu(w.t_first, contribs)
+    torch.cuda.synchronize()
+    for a, b, what in zip(fused_out, [case.master.cpu(), case.pout.cpu(), case.gout.cpu()],
+                          ("master", "param", "reduced grad")):
+        assert torch.equal(a, b), f"fused and separate routes differ: {what}"
+
+
 # ------------------------------------------------------------------ gather / reshard
 GATHER = [
     ([1000, 37, 4096, 3], 1500, 4),
@@ -681,6 +836,11 @@ DIM0_EDGE = [
     ([(129, 64), (1000,)], 64, 63, "compact", "shard"),
     ([(129, 64), (1000,), (2, 3)], 64, 5, "flat", "ag_slot"),
     ([(33, 17), (1,), (250, 40)], 3, 2, "flat", "ag_slot"),
+    # 75 tensors: three table launches mixing aligned and unaligned slices
+    ([((k * 7) % 41 + 1, (k * 5) % 13 + 1) if k % 9 else (64, 64) for k in range(75)],
+     4, 3, "flat", "ag_slot"),
+    ([((k * 7) % 41 + 1, (k * 5) % 13 + 1) if k % 9 else (64, 64) for k in range(75)],
+     8, 0, "compact", "ag_slot"),
 ]
 
 
@@ -704,6 +864,24 @@ def test_dim0_layout_steps_full_compare(shapes, n_d, rank, gl, om):
     pos = case.flat_pos if om == "ag_slot" else np.arange(case.S)
     assert_bitwise(u16(case.pout)[pos], case.o_p, "param")
     case.check_canaries(n_probe=4096)
+
+
+@pytest.mark.parametrize("launch", [(3, 64, 0), (0, 0, 1), (5000, 128, 0)])
+def test_dim0_launch_shape_invariance(launch):
+    shapes = [((k * 7) % 41 + 1, (k * 5) % 13 + 1) if k % 9 else (64, 64) for k in range(75)]
+    numel = [int(np.prod(s)) for s in shapes]
+    outs = []
+    for lc in (None, launch):
+        w = workloads.Workload("gpt2s_fsdp2", numel, 0, 4, 2, "flat", "ag_slot", 1, 1,
+                               ("normal", 1e-3), ("normal", 0.02), ("normal", 1e-4),
+                               ("absnormal", 1e-6), rows=[s[0] for s in shapes])
+        case = Case(w)
+        case.init_state_gpu()
+        case.step_gpu(2, case.grads_gpu(2), launch=lc)
+        torch.cuda.synchronize()
+        outs.append([case.master.cpu().numpy(), u16(case.pout), case.gout.cpu().numpy()])
+    for a, b in zip(*outs):
+        assert_bitwise(a, b, f"dim0 launch {launch}")
 
 
 @pytest.mark.timeout(600)
