@@ -47,6 +47,17 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def step_kernel_name(n_d: int, mapped: bool) -> str:
+    """The step_vec_kernel instantiation the library launches for bf16
+    contributions (its name in rocprofv3 traces): <N_d or 0 for the runtime
+    loop, flat addressing, ranks loaded per group, non-temporal, dtype 0>."""
+    nd = n_d if n_d in (2, 4, 8, 16, 32, 64) else 0
+    group = min(16, nd - 1) if nd > 1 else 1
+    nt = 2 * n_d >= 64
+    b = lambda x: "true" if x else "false"
+    return f"step_vec_kernel<{nd}, {b(mapped)}, {group}, {b(nt)}, 0>"
+
+
 def traffic_from_profiles(workload: str, n_launch_bytes: float):
     """Measured HBM bytes per launch from the committed counter summary, if it
     was taken on the current kernel sources; else None."""
@@ -60,27 +71,83 @@ def traffic_from_profiles(workload: str, n_launch_bytes: float):
     return d.get("hbm_bytes_per_launch")
 
 
-def build_inputs(z, synth, w, L):
+class Inputs:
+    """The buffers of one shard-step call: `grads` (N_d contributions),
+    `accs` (N_d fp32 accumulators, or None), `state` [master, m, v], `pout`."""
+
+    def __init__(self, views, n_d, pool=None):
+        self.grads = [views[f"g{q}"] for q in range(n_d)]
+        self.accs = [views[f"a{q}"] for q in range(n_d)] if "a0" in views else None
+        self.state = [views["master"], views["exp_avg"], views["exp_avg_sq"]]
+        self.pout = views["param_out"]
+        self.pool = pool
+
+
+TUNE_SLACK = 32 << 30   # extra pool bytes over which the tuned placement may shift
+
+
+def step_call(z, L, hp, t, grad_layout, out_mode, fused=False):
+    """views -> one step call on those buffers (for placement tuning)."""
+    def call(v):
+        nd = L.n_d
+        g = [v[f"g{q}"] for q in range(nd)]
+        st = (v["master"], v["exp_avg"], v["exp_avg_sq"], v["param_out"])
+        if fused:
+            z.zero_shard_step_accumulate(L, hp, t, [v[f"a{q}"] for q in range(nd)], g, 0.25,
+                                         z.DTYPE_BF16, grad_layout, *st[:3], st[3], out_mode)
+        else:
+            z.zero_shard_step(L, hp, t, g, grad_layout, *st[:3], st[3], out_mode)
+    return call
+
+
+def make_inputs(z, synth, w, L, placement="tuned", grad_dtype=None, accumulators=False,
+                grad_micro=0, call=None):
+    """Buffers for workload w on layout L filled with the workload's seeded
+    values (contributions keyed (grad, rank, grad_micro, t_first); FLAT ones
+    over the padded flat buffer), the output zeroed.  placement "tuned": one
+    pool laid out by zero_placement_plan with TUNE_SLACK spare bytes, the
+    arrangement's start chosen by timing `call` (views -> one call) at 4 GiB
+    shifts; "planned": the same pool without spare bytes; "separate": one
+    torch allocation per buffer."""
     import torch
+    from fsdp_sharded_optimizer_step_amd import placement as zp
     dev = torch.device("cuda:0")
-    buckets = L.buckets()
-    so, ln, po, pl, sh = (list(x) for x in zip(*buckets))
-    segs = synth.shard_segments(so, ln, pl, sh, w.n_d, w.rank)
-    S, P = L.shard, L.padded
-    grads = []
+    flat = w.grad_layout == "flat"
+    gl = z.GRAD_FLAT if flat else z.GRAD_COMPACT
+    om = z.OUT_AG_SLOT if w.out_mode == "ag_slot" else z.OUT_SHARD
+    specs = zp.step_specs(L, grad_dtype=grad_dtype, grad_layout=gl, out_mode=om,
+                          accumulators=accumulators)
+    if placement in ("tuned", "planned"):
+        choose = None
+        if placement == "tuned":
+            if call is None:
+                call = step_call(z, L, z.AdamW(**w.hp), w.t_first, gl, om, fused=accumulators)
+            timed = make_timer(torch.cuda.current_stream())
+            choose = lambda v: timed(lambda: call(v), reps=4)
+        pool = zp.Pool(specs, device=dev, slack=TUNE_SLACK if placement == "tuned" else 0,
+                       choose=choose)
+        views = pool.views
+    elif placement == "separate":
+        pool = None
+        views = {name: torch.empty(n, dtype=dt, device=dev) for name, n, dt, _ in specs}
+    else:
+        raise ValueError(placement)
+    so, ln, po, pln, sh = (list(x) for x in zip(*L.buckets()))
+    segs = synth.shard_segments(so, ln, pln, sh, w.n_d, w.rank)
+    gsegs = [(p0, s0, l, pl - l) for s0, l, p0, pl in zip(so, ln, po, pln)] if flat else segs
+    gdist = w.micro_grad if w.n_micro else w.grad
     for q in range(w.n_d):
-        g = torch.empty(S, dtype=torch.int16, device=dev)
-        synth.fill_device(g, segs, synth.key(w.name, "grad", q, 0, w.t_first), *w.grad)
-        grads.append(g)
-    state = []
-    for kind, dist in (("master", w.master), ("exp_avg", w.exp_avg),
-                       ("exp_avg_sq", w.exp_avg_sq)):
-        b = torch.empty(S, dtype=torch.float32, device=dev)
-        synth.fill_device(b, segs, synth.key(w.name, kind), *dist)
-        state.append(b)
-    pout = torch.zeros(P if w.out_mode == "ag_slot" else S, dtype=torch.int16, device=dev)
+        synth.fill_device(views[f"g{q}"], gsegs,
+                          synth.key(w.name, "grad", q, grad_micro, w.t_first), *gdist)
+        if accumulators:
+            synth.fill_device(views[f"a{q}"], gsegs, synth.key(w.name, "grad", q, 0, w.t_first),
+                              *gdist)
+    for kind, dist, name in (("master", w.master, "master"), ("exp_avg", w.exp_avg, "exp_avg"),
+                             ("exp_avg_sq", w.exp_avg_sq, "exp_avg_sq")):
+        synth.fill_device(views[name], segs, synth.key(w.name, kind), *dist)
+    views["param_out"].zero_()
     torch.cuda.synchronize()
-    return grads, state, pout, segs
+    return Inputs(views, w.n_d, pool), segs
 
 
 def cpu_baseline(w, segs, S, target_s=12.0):
@@ -252,11 +319,11 @@ def aux_kernels(z, synth, workloads):
     return out
 
 
-def next_rows(z, synth, w, L, grads, state, pout, timed):
-    """The rows beyond the bf16 step, measured on the same llama8b-sized
-    buffers: FSDP2 (dim-0) step, parameter gather, fp32-contribution step,
-    the step with the last micro-batch folded in and the 8 -> 4 rank state
-    re-cut.  Consumes `grads` (freed here)."""
+def next_rows(z, synth, w, L, holder, timed, placement):
+    """The rows beyond the bf16 step, measured on llama8b-sized buffers:
+    FSDP2 (dim-0) step, parameter gather, fp32-contribution step, the step
+    with the last micro-batch folded in and the 8 -> 4 rank state re-cut.
+    holder[0]: the bench's inputs (released here)."""
     import torch
     dev = torch.device("cuda:0")
     S, P = L.shard, L.padded
@@ -268,112 +335,84 @@ def next_rows(z, synth, w, L, grads, state, pout, timed):
                     "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
                     "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
 
-    master, m, v = state
+    inp = holder.pop()
     # FSDP2 per-parameter layout, ZeRO-3 in place (COMPACT contributions)
     rows = [sh[1][0] for sh in w.shapes]
     Ld = z.Layout(w.numel, 0, w.n_d, w.rank, rows=rows)
     assert Ld.shard == S
-    shard_out = pout[:S]
-    ms = timed(lambda: z.zero_shard_step(Ld, hp, 5, grads, z.GRAD_COMPACT, master, m, v,
+    shard_out = inp.pout[:S]
+    ms = timed(lambda: z.zero_shard_step(Ld, hp, 5, inp.grads, z.GRAD_COMPACT, *inp.state,
                                          shard_out, z.OUT_SHARD))
     row("fsdp2_step", "step_vec_kernel", "llama8b_fsdp2: Llama-3-8B per-parameter dim-0 "
         "layout, N_d=8, rank 7, in place", S * (2 * w.n_d + 26), ms)
     # All-Gather local part: the 8 bf16 shards (the contribution buffers
     # stand in for them) into the 8.03e9-element flat buffer
-    ms = timed(lambda: z.zero_gather_params(L, grads, pout))
-    row("gather", "gather_vec_kernel", "llama8b: 8 rank shards -> 8,030,261,248-element flat "
+    ms = timed(lambda: z.zero_gather_params(L, inp.grads, inp.pout))
+    row("gather", "gather_kernel", "llama8b: 8 rank shards -> 8,030,261,248-element flat "
         "buffer", 4 * P, ms)
-    del grads[:]
+    del inp, shard_out
     torch.cuda.empty_cache()
     # fp32 contributions
-    g32 = []
-    so, ln, _, pln, sh = (list(x) for x in zip(*L.buckets()))
-    segs = synth.shard_segments(so, ln, pln, sh, w.n_d, w.rank)
-    for q in range(w.n_d):
-        g = torch.empty(S, dtype=torch.float32, device=dev)
-        synth.fill_device(g, segs, synth.key(w.name, "grad", q, 0, w.t_first), *w.grad)
-        g32.append(g)
-    ms = timed(lambda: z.zero_shard_step(L, hp, 7, g32, z.GRAD_COMPACT, master, m, v, pout,
-                                         z.OUT_AG_SLOT))
+    inp, _ = make_inputs(z, synth, w, L, placement, grad_dtype=torch.float32)
+    ms = timed(lambda: z.zero_shard_step(L, hp, 7, inp.grads, z.GRAD_COMPACT, *inp.state,
+                                         inp.pout, z.OUT_AG_SLOT))
     row("step_f32", "step_vec_kernel (fp32 contributions)", "llama8b with fp32 contributions "
         "(4*N_d+26 = 58 B/elem)", S * (4 * w.n_d + 26), ms)
-    # the last no_sync micro-batch folded into the step: the fp32 buffers
-    # stand in for the ranks' accumulators, plus one bf16 micro-batch each
-    micro = []
-    for q in range(w.n_d):
-        g = torch.empty(S, dtype=torch.int16, device=dev)
-        synth.fill_device(g, segs, synth.key(w.name, "grad", q, 1, w.t_first), *w.grad)
-        micro.append(g)
-    ms = timed(lambda: z.zero_shard_step_accumulate(L, hp, 8, g32, micro, 0.25, z.DTYPE_BF16,
-                                                    z.GRAD_COMPACT, master, m, v, pout,
-                                                    z.OUT_AG_SLOT))
+    del inp
+    torch.cuda.empty_cache()
+    # the last no_sync micro-batch folded into the step: each rank's fp32
+    # accumulator plus its bf16 micro-batch
+    inp, _ = make_inputs(z, synth, w, L, placement, accumulators=True, grad_micro=1)
+    ms = timed(lambda: z.zero_shard_step_accumulate(L, hp, 8, inp.accs, inp.grads, 0.25,
+                                                    z.DTYPE_BF16, z.GRAD_COMPACT, *inp.state,
+                                                    inp.pout, z.OUT_AG_SLOT))
     row("step_fused_accumulate", "step_vec_kernel (accumulator + last micro-batch)",
         "llama8b, each rank's contribution = bf16(acc + micro/4) inside the step "
         "(6*N_d+26 = 74 B/elem)", S * (6 * w.n_d + 26), ms)
-    del micro
-    torch.cuda.empty_cache()
-    # re-cut one fp32 state array saved from 8 ranks for 4 ranks (the fp32
-    # buffers stand in for the 8 saved shards)
+    # re-cut one fp32 state array saved from 8 ranks for 4 ranks (the
+    # accumulators stand in for the 8 saved shards)
     L4 = z.Layout(w.numel, w.cap, 4, 3)
     dst = torch.empty(L4.shard, dtype=torch.float32, device=dev)
-    ms = timed(lambda: z.zero_reshard(L, g32, L4, dst), reps=5)
+    ms = timed(lambda: z.zero_reshard(L, inp.accs, L4, dst), reps=5)
     row("reshard", "reshard_kernel<u32>", "llama8b fp32 state: 8 ranks -> rank 3 of 4 "
         f"({L4.shard} elements)", 8 * L4.shard, ms)
-    del g32, dst
+    del inp, dst
     torch.cuda.empty_cache()
     return out
 
 
-def all_configs(z, synth, workloads, steps, warmup):
+def all_configs(z, synth, workloads, steps, warmup, placement):
     """Step time of every shard workload (inputs resident, HIP events on the
-    launch stream); FLAT workloads read their contributions from N_d packed
+    launch stream); FLAT workloads read their contributions from N_d padded
     flat buffers, the others from N_d shard-ordered buffers."""
     import torch
-    dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     timed = make_timer(stream)
     res = []
     for name in workloads.NAMES + workloads.DIM0_NAMES:
         w = workloads.get(name)
         L = z.Layout(w.numel, w.cap, w.n_d, w.rank, rows=w.rows)
-        S, P = L.shard, L.padded
-        so, ln, _, pln, sh = (list(x) for x in zip(*L.buckets()))
-        segs = synth.shard_segments(so, ln, pln, sh, w.n_d, w.rank)
-        gdist = w.micro_grad if w.n_micro else w.grad
-        grads = []
-        for q in range(w.n_d):
-            if w.grad_layout == "compact":
-                g = torch.empty(S, dtype=torch.int16, device=dev)
-                synth.fill_device(g, segs, synth.key(w.name, "grad", q, 0, w.t_first), *gdist)
-            else:
-                g = torch.empty(P, dtype=torch.int16, device=dev)
-                flat_segs = [(po, s0, l, pl - l) for s0, l, po, pl in
-                             zip(so, ln, [b[2] for b in L.buckets()], pln)]
-                synth.fill_device(g, flat_segs, synth.key(w.name, "grad", q, 0, w.t_first),
-                                  *gdist)
-            grads.append(g)
-        state = []
-        for kind, dist in (("master", w.master), ("exp_avg", w.exp_avg),
-                           ("exp_avg_sq", w.exp_avg_sq)):
-            b = torch.empty(S, dtype=torch.float32, device=dev)
-            synth.fill_device(b, segs, synth.key(w.name, kind), *dist)
-            state.append(b)
-        pout = torch.zeros(P if w.out_mode == "ag_slot" else S, dtype=torch.int16, device=dev)
+        S = L.shard
+        inp, _ = make_inputs(z, synth, w, L, placement)
         hp = z.AdamW(**w.hp)
         gl = z.GRAD_COMPACT if w.grad_layout == "compact" else z.GRAD_FLAT
         om = z.OUT_AG_SLOT if w.out_mode == "ag_slot" else z.OUT_SHARD
+
+        def call():
+            z.zero_shard_step(L, hp, w.t_first, inp.grads, gl, *inp.state, inp.pout, om)
+
         for _ in range(warmup):
-            z.zero_shard_step(L, hp, w.t_first, grads, gl, *state, pout, om)
-        ms = timed(lambda: z.zero_shard_step(L, hp, w.t_first, grads, gl, *state, pout, om),
-                   reps=steps)
+            call()
+        ms = timed(call, reps=steps)
         nbytes = S * (2 * w.n_d + 26)
         res.append({"workload": name, "shard_elems": S, "n_d": w.n_d, "buckets": L.n_buckets,
-                    "grad_layout": w.grad_layout, "out_mode": w.out_mode, "ms": ms,
+                    "grad_layout": w.grad_layout, "out_mode": w.out_mode,
+                    "placement": placement, "ms": ms,
                     "Gelem_per_s": S / (ms * 1e-3) / 1e9, "GBps": nbytes / (ms * 1e-3) / 1e9,
                     "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
         print(f"# {name}: S={S} {ms:.4f} ms {res[-1]['GBps']:.0f} GB/s", file=sys.stderr,
               flush=True)
-        del grads, state, pout
+        del inp
         torch.cuda.empty_cache()
     return res
 
@@ -388,6 +427,10 @@ def main():
     ap.add_argument("--no-aux", action="store_true", help="skip the pack/accumulate timings")
     ap.add_argument("--blocks", type=int, default=0)
     ap.add_argument("--threads", type=int, default=0)
+    ap.add_argument("--placement", default="tuned", choices=["tuned", "planned", "separate"],
+                    help="tuned: the step's buffers in one pool laid out by zero_placement_plan, "
+                         "its start chosen by timing the step at a few shifts; planned: the "
+                         "same pool at shift 0; separate: one torch allocation per buffer")
     ap.add_argument("--all-configs", action="store_true",
                     help="time the step of every shard workload instead (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -418,14 +461,14 @@ def main():
     z.load()
     if args.all_configs:
         print(json.dumps({"per_config": all_configs(z, synth, workloads, args.steps,
-                                                    args.warmup)}), flush=True)
+                                                    args.warmup, args.placement)}), flush=True)
         return
     w = workloads.get(args.workload)
     L = z.Layout(w.numel, w.cap, w.n_d, w.rank)
     S, P = L.shard, L.padded
     print(f"# workload {w.name}: S={S} P={P} N_d={w.n_d} buckets={L.n_buckets}", file=sys.stderr,
           flush=True)
-    grads, (master, m, v), pout, segs = build_inputs(z, synth, w, L)
+    inp, segs = make_inputs(z, synth, w, L, args.placement)
     hp = z.AdamW(**w.hp)
     gl = z.GRAD_COMPACT if w.grad_layout == "compact" else z.GRAD_FLAT
     om = z.OUT_AG_SLOT if w.out_mode == "ag_slot" else z.OUT_SHARD
@@ -433,7 +476,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(t):
-        z.zero_shard_step(L, hp, t, grads, gl, master, m, v, pout, om, launch=launch,
+        z.zero_shard_step(L, hp, t, inp.grads, gl, *inp.state, inp.pout, om, launch=launch,
                           stream=stream)
 
     t = w.t_first
@@ -466,13 +509,33 @@ def main():
     # the same byte mix with trivial arithmetic, on the bench's own buffers
     # (after the timed region: it overwrites the state)
     import measure
-    ceil_gbps, ceil_cfg = measure.stream_ceiling(grads, [master, m, v], pout, S)
+    ceil_gbps, ceil_cfg = measure.stream_ceiling(inp.grads, inp.state, inp.pout, S)
     print(f"# same-mix streaming ceiling: {ceil_gbps:.0f} GB/s {ceil_cfg}", file=sys.stderr,
           flush=True)
     nxt = []
+    tuning = None
+    if inp.pool is not None:
+        tuning = {"pool_GiB": inp.pool.nbytes / 2**30, "chosen_shift_GiB": inp.pool.shift / 2**30,
+                  "ms_by_shift_GiB": [[sh / 2**30, ms] for sh, ms in inp.pool.tuning]}
+    holder = [inp]
+    del inp
     if not args.no_aux and w.name == "llama8b":
-        nxt = next_rows(z, synth, w, L, grads, [master, m, v], pout, make_timer(stream))
-    del grads
+        nxt = next_rows(z, synth, w, L, holder, make_timer(stream), args.placement)
+    holder.clear()
+    torch.cuda.empty_cache()
+    # the same step on one torch allocation per buffer, for comparison
+    other = None
+    if not args.no_aux:
+        alt = "separate" if args.placement != "separate" else "tuned"
+        inp, _ = make_inputs(z, synth, w, L, alt)
+        ms_alt = make_timer(stream)(lambda: z.zero_shard_step(L, hp, t, inp.grads, gl, *inp.state,
+                                                              inp.pout, om), reps=10)
+        other = {"placement": alt, "kernel_avg_ms": ms_alt,
+                 "GBps": alg_bytes / (ms_alt * 1e-3) / 1e9,
+                 "frac": alg_bytes / (ms_alt * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        print(f"# placement {alt}: {ms_alt:.3f} ms, {other['GBps']:.0f} GB/s", file=sys.stderr,
+              flush=True)
+        del inp
     torch.cuda.empty_cache()
     aux = nxt + ([] if args.no_aux else aux_kernels(z, synth, workloads))
     for a in aux:
@@ -499,16 +562,20 @@ def main():
         "config": {"workload": w.name, "description": WORKLOAD_LABEL[w.name], "shard_elems": S,
                    "padded_elems": P, "n_d": w.n_d, "rank": w.rank, "buckets": L.n_buckets,
                    "grad_layout": w.grad_layout, "out_mode": w.out_mode,
-                   "bytes_per_elem": bytes_per_elem, "io": "bf16 grads and params, f32 state"},
+                   "bytes_per_elem": bytes_per_elem, "io": "bf16 grads and params, f32 state",
+                   "placement": args.placement, "placement_tuning": tuning},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "kernel": "step_vec_kernel", "kernel_avg_ms": k_avg,
+                     "kernel": step_kernel_name(w.n_d, w.grad_layout == "flat"
+                                                or w.out_mode == "ag_slot"),
+                     "kernel_avg_ms": k_avg,
                      "algorithmic_bytes_per_launch": alg_bytes, "kernel_hash": kernel_hash()},
         "cpu_baseline": cpu,
         "same_mix_ceiling": {"GBps": ceil_gbps, "frac_of_peak": ceil_gbps / PEAK_HBM_GBPS,
                              "step_frac_of_ceiling": achieved / ceil_gbps,
                              "kernel": "measure/stream_ceiling.hip: the step's bytes, "
                                        "trivial arithmetic", "best_config": ceil_cfg},
+        "placement_comparison": other,
         "aux_kernels": aux,
     }
     print(json.dumps(out), flush=True)

@@ -27,7 +27,7 @@ EXPORTS = ("zero_layout_create", "zero_layout_destroy", "zero_layout_psi", "zero
            "zero_layout_bucket", "zero_layout_tensor", "zero_bucket_pack", "zero_grad_accumulate",
            "zero_shard_step", "zero_shard_step_ex", "zero_step_scalars", "zero_strerror",
            "zero_gather_params", "zero_reshard", "zero_layout_create_dim0", "zero_layout_kind",
-           "zero_shard_step_accumulate")
+           "zero_shard_step_accumulate", "zero_placement_plan")
 
 
 class ZeroError(RuntimeError):
@@ -94,6 +94,8 @@ def load():
     lib.zero_gather_params.argtypes = [vp, C.POINTER(vp), C.c_int64, C.c_int64, vp, vp]
     lib.zero_reshard.argtypes = [vp, C.POINTER(vp), vp, vp, C.c_int32, vp]
     lib.zero_step_scalars.argtypes = [C.POINTER(_AdamW), C.c_int64, C.POINTER(C.c_float)]
+    lib.zero_placement_plan.argtypes = [C.c_int32, _i64p, C.POINTER(C.c_double), C.c_int64,
+                                        C.c_int32, C.c_int64, _i64p, _i64p]
     lib.zero_strerror.argtypes = [C.c_int]
     lib.zero_strerror.restype = C.c_char_p
     _lib = lib
@@ -296,3 +298,17 @@ def zero_step_scalars(hp: AdamW, t: int):
     out = (C.c_float * 8)()
     _check("zero_step_scalars", load().zero_step_scalars(C.byref(hp._c()), t, out))
     return list(out)
+
+
+def zero_placement_plan(nbytes, traffic, lane_bytes: int, n_lanes: int, align: int):
+    """Byte offsets of the buffers inside one pool, and the pool size."""
+    n = len(nbytes)
+    if len(traffic) != n:
+        raise ValueError("zero_placement_plan: one traffic figure per buffer is required")
+    nb = (C.c_int64 * max(1, n))(*[int(x) for x in nbytes])
+    tr = (C.c_double * max(1, n))(*[float(x) for x in traffic])
+    offs = (C.c_int64 * max(1, n))()
+    total = C.c_int64()
+    _check("zero_placement_plan", load().zero_placement_plan(
+        n, nb, tr, int(lane_bytes), int(n_lanes), int(align), offs, C.byref(total)))
+    return [int(offs[k]) for k in range(n)], int(total.value)

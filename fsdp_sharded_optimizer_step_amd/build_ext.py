@@ -7,7 +7,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libzero_shard.so")
-SOURCES = ["layout.cpp", "shard_step.hip", "pack_accumulate.hip", "gather_reshard.hip"]
+SOURCES = ["layout.cpp", "placement.cpp", "shard_step.hip", "pack_accumulate.hip",
+           "gather_reshard.hip"]
 
 # Floating point: no contraction into FMA, correctly rounded binary32 divide
 # and square root, subnormals kept (no flush), no fast-math.  Packed fp32

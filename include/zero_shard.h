@@ -329,6 +329,39 @@ int zero_reshard(const zero_layout* src, const void* const* src_shards_dev,
                  const zero_layout* dst, void* dst_shard_dev, int32_t elem_bytes,
                  hipStream_t stream);
 
+/* -------------------------------------------------------------- placement
+ * Host-only planner for placing the step's buffers inside ONE device
+ * allocation that the caller makes (the library allocates nothing).
+ *
+ * Why: every call streams all its buffers once, so its speed is set by how
+ * HBM serves the concurrent streams.  Measured on MI355X (288 GB HBM3E), the
+ * same buffers run up to ~15 % faster or slower depending on their position
+ * in memory (a pattern with a 96 GiB period); buffers spread round-robin over
+ * three lanes 32 GiB apart, each lane carrying a third of the traffic per
+ * element, ran at the fast end at every shift tried.  The results of every
+ * entry point are the same for any placement.
+ *
+ * Buffer k has nbytes[k] bytes and moves traffic[k] bytes of HBM traffic per
+ * shard element (e.g. 2 for a bf16 contribution, 8 for an fp32 state array
+ * that is read and written, 2 for the bf16 output).  Buffers are assigned to
+ * n_lanes classes so that the classes carry equal traffic (heaviest first,
+ * each to the least loaded class, ties to the lower class); class c then
+ * packs its buffers, in list order and each aligned to `align`, into lane
+ * slots at offsets (c + j*n_lanes) * lane_bytes, j = 0, 1, ...  A buffer
+ * larger than lane_bytes is placed after all others.  offsets_out[k]
+ * receives buffer k's byte offset in the pool, *pool_bytes_out the pool
+ * size to allocate.  No two buffers overlap.
+ *
+ * Suggested values on MI355X: lane_bytes = 32 GiB, n_lanes = 3,
+ * align = 2 MiB.  nbytes/traffic/offsets_out: host arrays of n entries.
+ * Errors: ZERO_EINVAL (null pointer with n > 0, negative size, traffic not
+ * finite or negative, n_lanes outside [1, 64], align not a power of two of
+ * at least 16, lane_bytes not a positive multiple of align), ZERO_ERANGE
+ * (sizes beyond 2^62 bytes). */
+int zero_placement_plan(int32_t n, const int64_t* nbytes, const double* traffic,
+                        int64_t lane_bytes, int32_t n_lanes, int64_t align,
+                        int64_t* offsets_out, int64_t* pool_bytes_out);
+
 /* Per-call binary32 scalars for step t, in the order
  * {s, rho, a_wd, B1, C1, B2, C2, E}.  Errors: ZERO_EINVAL. */
 int zero_step_scalars(const zero_adamw* hp, int64_t t, float out[8]);

@@ -259,3 +259,89 @@ def test_accumulate_and_pack_argument_errors():
     ov = (C.c_void_p * 2)(0x10000, 0x20000 + 6)
     assert lib.zero_bucket_pack(L.handle, ov, 0, 4, 0x20000, None) == E.ZERO_EOVERLAP
     assert lib.zero_bucket_pack(L.handle, arr, 1, 1, 0x20000, None) == E.ZERO_OK
+
+
+# ------------------------------------------------------------------ placement planner
+def _classes(offs, lane, n_lanes):
+    return [(o // lane) % n_lanes for o in offs]
+
+
+def _check_plan(nbytes, traffic, lane, n_lanes, align):
+    offs, total = binding.zero_placement_plan(nbytes, traffic, lane, n_lanes, align)
+    iv = sorted((o, o + n) for o, n in zip(offs, nbytes))
+    assert all(a[1] <= b[0] for a, b in zip(iv, iv[1:])), "buffers overlap"
+    assert all(o % align == 0 for o in offs)
+    assert total == (max(o + n for o, n in zip(offs, nbytes)) if nbytes else 0)
+    for o, n in zip(offs, nbytes):
+        if n <= lane:   # a buffer that fits a lane stays inside one lane slot
+            assert o // lane == (o + n - 1) // lane or n == 0
+    return offs, total
+
+
+def test_placement_plan_spreads_the_llama8b_step_over_three_lanes():
+    """Contributions (2 B/elem each), fp32 state (8 B/elem each) and the bf16
+    output (2 B/elem): the three 32 GiB lane classes carry 14 B/elem each."""
+    S, P, GiB = 1_003_782_656, 8_030_261_248, 1 << 30
+    for out_bytes in (2 * P, 2 * S):
+        nbytes = [2 * S] * 8 + [4 * S] * 3 + [out_bytes]
+        traffic = [2.0] * 8 + [8.0] * 3 + [2.0]
+        offs, total = _check_plan(nbytes, traffic, 32 * GiB, 3, 2 << 20)
+        load = [0.0] * 3
+        for c, t in zip(_classes(offs, 32 * GiB, 3), traffic):
+            load[c] += t
+        assert load == [14.0, 14.0, 14.0]
+        # the three state arrays land in three different lanes
+        assert sorted(_classes(offs[8:11], 32 * GiB, 3)) == [0, 1, 2]
+        assert total < 96 * GiB
+
+
+def test_placement_plan_llama70b_and_edge_cases():
+    S, GiB = 1_102_401_664, 1 << 30
+    nbytes = [2 * S] * 64 + [4 * S] * 3 + [2 * S]
+    traffic = [2.0] * 64 + [8.0] * 3 + [2.0]
+    offs, total = _check_plan(nbytes, traffic, 32 * GiB, 3, 2 << 20)
+    load = [0.0] * 3
+    for c, t in zip(_classes(offs, 32 * GiB, 3), traffic):
+        load[c] += t
+    assert max(load) - min(load) <= 2.0
+    # deterministic
+    assert binding.zero_placement_plan(nbytes, traffic, 32 * GiB, 3, 2 << 20) == (offs, total)
+    # a buffer larger than a lane goes after the others
+    offs, total = _check_plan([100, 5000, 30], [1.0, 1.0, 1.0], 1024, 3, 16)
+    assert offs[1] >= max(offs[0] + 100, offs[2] + 30)
+    # one lane: packed in list order
+    offs, _ = _check_plan([100, 50, 70], [1.0, 9.0, 3.0], 4096, 1, 16)
+    assert offs == [0, 112, 176]
+    # nothing to place
+    assert binding.zero_placement_plan([], [], 1024, 3, 16) == ([], 0)
+    # zero-sized buffers are allowed
+    _check_plan([0, 64, 0], [1.0, 2.0, 0.0], 1024, 3, 16)
+
+
+def test_placement_plan_errors():
+    lib = z.load()
+    E = z.binding
+    nb = (C.c_int64 * 2)(10, 20)
+    tr = (C.c_double * 2)(1.0, 2.0)
+    offs = (C.c_int64 * 2)()
+    tot = C.c_int64()
+
+    def call(n=2, nbytes=nb, traffic=tr, lane=1024, lanes=3, align=16, o=offs, t=C.byref(tot)):
+        return lib.zero_placement_plan(n, nbytes, traffic, lane, lanes, align, o, t)
+
+    assert call() == E.ZERO_OK
+    assert call(n=-1) == E.ZERO_EINVAL
+    assert call(nbytes=None) == E.ZERO_EINVAL
+    assert call(o=None) == E.ZERO_EINVAL
+    assert call(t=None) == E.ZERO_EINVAL
+    assert call(lanes=0) == E.ZERO_EINVAL
+    assert call(lanes=65) == E.ZERO_EINVAL
+    assert call(align=24) == E.ZERO_EINVAL
+    assert call(align=8) == E.ZERO_EINVAL
+    assert call(lane=1000) == E.ZERO_EINVAL
+    assert call(lane=0) == E.ZERO_EINVAL
+    assert call(traffic=(C.c_double * 2)(1.0, float("nan"))) == E.ZERO_EINVAL
+    assert call(traffic=(C.c_double * 2)(-1.0, 1.0)) == E.ZERO_EINVAL
+    assert call(nbytes=(C.c_int64 * 2)(-5, 1)) == E.ZERO_EINVAL
+    assert call(nbytes=(C.c_int64 * 2)(1 << 62, 1)) == E.ZERO_ERANGE
+    assert call(n=0, nbytes=None, traffic=None, o=None) == E.ZERO_OK and tot.value == 0

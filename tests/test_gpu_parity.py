@@ -221,6 +221,41 @@ def test_edge_cases_full_compare(numel, cap, n_d, rank, gl, om):
     case.check_canaries(n_probe=4096)
 
 
+@pytest.mark.parametrize("gl,om", [("flat", "ag_slot"), ("compact", "shard")])
+def test_planned_placement_gives_identical_results(gl, om):
+    """The step on buffers carved from one pool laid out by
+    zero_placement_plan (lanes of 1 MiB here, so the lane structure is
+    exercised at a small size) equals the step on separate allocations."""
+    from fsdp_sharded_optimizer_step_amd import placement as zp
+    case = _edge_case([300_001, 77], 65_536, 8, 5, gl, om)
+    case.init_state_gpu()
+    grads = case.grads_gpu(2)
+    # the shift is chosen by a timing callback; this one makes the last of
+    # the three candidate shifts (0, 1, 2 MiB) the fastest
+    times = iter([3.0, 2.0, 1.0])
+    pool = zp.step_pool(case.L, grad_layout=z.GRAD_FLAT if gl == "flat" else z.GRAD_COMPACT,
+                        out_mode=z.OUT_AG_SLOT if om == "ag_slot" else z.OUT_SHARD,
+                        reduced_grad=True, lane_bytes=1 << 20, n_lanes=3, align=256,
+                        slack=2 << 20, choose=lambda views: next(times), shift_step=1 << 20)
+    assert [sh for sh, _ in pool.tuning] == [0, 1 << 20, 2 << 20] and pool.shift == 2 << 20
+    assert len({(o - pool.shift) // (1 << 20) % 3 for o in pool.offsets.values()}) == 3
+    assert pool["master"].data_ptr() == pool.buf.data_ptr() + pool.offsets["master"]
+    for q, g in enumerate(grads):
+        pool[f"g{q}"].copy_(g)
+    for name, t in (("master", case.master), ("exp_avg", case.m), ("exp_avg_sq", case.v),
+                    ("param_out", case.pout)):
+        pool[name].copy_(t)
+    case.step_gpu(2, grads)
+    z.zero_shard_step(case.L, case.hp_z, 2, [pool[f"g{q}"] for q in range(8)],
+                      z.GRAD_FLAT if gl == "flat" else z.GRAD_COMPACT, pool["master"],
+                      pool["exp_avg"], pool["exp_avg_sq"], pool["param_out"],
+                      z.OUT_AG_SLOT if om == "ag_slot" else z.OUT_SHARD, pool["reduced_grad"])
+    torch.cuda.synchronize()
+    for name, t in (("master", case.master), ("exp_avg", case.m), ("exp_avg_sq", case.v),
+                    ("param_out", case.pout), ("reduced_grad", case.gout)):
+        assert torch.equal(pool[name].cpu(), t.cpu()), name
+
+
 def test_empty_shard_is_a_no_op():
     L = z.Layout([], 0, 4, 0)
     e = torch.empty(0, dtype=torch.float32, device=DEV)
