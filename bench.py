@@ -192,11 +192,24 @@ def cpu_baseline(w, segs, S, target_s=12.0):
     for k in range(reps):
         oracle.shard_step(G, *st, hp, w.t_first + k, nthreads=threads)
     dt = time.perf_counter() - t0
+    # one host thread on the first 2^22 elements of the same sample, about 3 s
+    n1 = min(n, 1 << 22)
+    G1, st1 = [g[:n1].copy() for g in G], [x[:n1].copy() for x in st]
     del G, st
+    t0 = time.perf_counter()
+    oracle.shard_step(G1, *st1, hp, w.t_first, nthreads=1)
+    pilot1 = max(1e-6, time.perf_counter() - t0)
+    reps1 = max(1, int(round(3.0 / pilot1)))
+    t0 = time.perf_counter()
+    for k in range(reps1):
+        oracle.shard_step(G1, *st1, hp, w.t_first + 1 + k, nthreads=1)
+    dt1 = time.perf_counter() - t0
     return {"value": n * reps / dt, "unit": "elem/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} elements of the same shard (inputs generated untimed), "
                       f"{reps} consecutive steps, {dt:.1f} s on {threads} host threads",
-            "gbps": n * reps * (2 * w.n_d + 26) / dt / 1e9}
+            "gbps": n * reps * (2 * w.n_d + 26) / dt / 1e9,
+            "single_thread": {"value": n1 * reps1 / dt1, "unit": "elem/s", "cores": 1,
+                              "sample": f"first {n1} elements, {reps1} steps, {dt1:.1f} s"}}
 
 
 def make_timer(stream):
@@ -217,91 +230,110 @@ def make_timer(stream):
     return timed
 
 
-def aux_kernels(z, synth, workloads):
-    """Pack (gpt2s list, one rank's 124M-element flat buffer) and the no_sync
-    accumulate sequence (accum1p3b shard: 4 calls) timed with HIP events."""
+def aux_kernels(z, synth, workloads, placement):
+    """Pack (gpt2s list, one rank's 124M-element flat buffer), the no_sync
+    accumulate sequence (accum1p3b shard: 4 calls for one rank) and the whole
+    accum1p3b job (8 ranks accumulate, then the step; the last accumulate
+    separate or folded into the step), timed with HIP events.  With a pool
+    placement the buffers of each measurement share one tuned pool."""
     import torch
+    from fsdp_sharded_optimizer_step_amd import placement as zp
     dev = torch.device("cuda:0")
     out = []
-    stream = torch.cuda.current_stream()
+    timed = make_timer(torch.cuda.current_stream())
 
-    timed = make_timer(stream)
+    def buffers(specs, call):
+        """name -> view (pool) or tensor (separate); `call(views)` is timed to
+        choose the pool's start."""
+        if placement == "separate":
+            return {n: torch.zeros(k, dtype=dt, device=dev) for n, k, dt, _ in specs}
+        pool = zp.Pool(specs, device=dev, slack=TUNE_SLACK if placement == "tuned" else 0,
+                       choose=(lambda v: timed(lambda: call(v), reps=3))
+                       if placement == "tuned" else None)
+        return pool.views
 
+    def record(kernel, desc, nbytes, ms):
+        out.append({"kernel": kernel, "workload": desc, "bytes_per_call": nbytes, "ms": ms,
+                    "GBps": nbytes / (ms * 1e-3) / 1e9,
+                    "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
+
+    # bucket pack: every tensor is read while the flat buffer is written
     w = workloads.get("gpt2s")
     L = z.Layout(w.numel, w.cap, w.n_d, w.rank)
-    tens = [torch.empty(n, dtype=torch.int16, device=dev) for n in w.numel]
-    for t, segs in zip(tens, synth.tensor_segments(w.numel)):
-        synth.fill_device(t, segs, synth.key(w.name, "grad", 0, 0, 1), *w.grad)
-    flat = torch.empty(L.padded, dtype=torch.int16, device=dev)
-    ms = timed(lambda: z.zero_bucket_pack(L, tens, flat))
-    nbytes = 2 * L.psi + 2 * L.padded
-    out.append({"kernel": "pack_kernel", "workload": "gpt2s: 148 tensors -> 124,439,808-element "
-                "flat buffer, 25 MiB buckets", "bytes_per_call": nbytes, "ms": ms,
-                "GBps": nbytes / (ms * 1e-3) / 1e9, "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
-    del tens, flat
+    specs = [(f"t{k}", n, torch.int16, float(n)) for k, n in enumerate(w.numel)]
+    specs += [("flat", L.padded, torch.int16, float(L.padded))]
+    nt = len(w.numel)
+    pack = lambda v: z.zero_bucket_pack(L, [v[f"t{k}"] for k in range(nt)], v["flat"])
+    v = buffers(specs, pack)
+    for k, segs in enumerate(synth.tensor_segments(w.numel)):
+        synth.fill_device(v[f"t{k}"], segs, synth.key(w.name, "grad", 0, 0, 1), *w.grad)
+    record("pack_kernel", "gpt2s: 148 tensors -> 124,439,808-element flat buffer, 25 MiB "
+           "buckets", 2 * L.psi + 2 * L.padded, timed(lambda: pack(v)))
+    del v
+    torch.cuda.empty_cache()
 
+    # one rank's no_sync sequence on the accum1p3b shard
     w = workloads.get("accum1p3b")
     L = z.Layout(w.numel, w.cap, w.n_d, w.rank)
     S = L.shard
-    acc = torch.empty(S, dtype=torch.float32, device=dev)
-    micro = [torch.empty(S, dtype=torch.int16, device=dev) for _ in range(w.n_micro)]
     so, ln, _, pln, sh = (list(x) for x in zip(*L.buckets()))
     segs = synth.shard_segments(so, ln, pln, sh, w.n_d, w.rank)
-    for k, mg in enumerate(micro):
-        synth.fill_device(mg, segs, synth.key(w.name, "micro_grad", 0, k, w.t_first), *w.micro_grad)
-    emit = torch.empty(S, dtype=torch.int16, device=dev)
+    scale = 1.0 / w.n_micro
+    nm, nd = w.n_micro, w.n_d
 
-    def seq():
-        for k in range(w.n_micro):
-            last = k == w.n_micro - 1
+    def seq(v):
+        for k in range(nm):
+            last = k == nm - 1
             flags = (z.ACC_OVERWRITE if k == 0 else 0) | (
                 z.ACC_EMIT_BF16 | z.ACC_NO_STORE if last else 0)
-            z.zero_grad_accumulate(acc, micro[k], 1.0 / w.n_micro, flags, emit if last else None)
+            z.zero_grad_accumulate(v["acc"], v[f"m{k}"], scale, flags, v["emit"] if last else None)
 
-    ms = timed(seq, reps=5)
-    nbytes = S * (6 + 10 + 10 + 8)
-    out.append({"kernel": "accum_vec_kernel", "workload": "accum1p3b: 162,500,000-element shard, "
-                "4 micro-batches (overwrite, add, add, add+emit bf16 without fp32 store)",
-                "bytes_per_call": nbytes, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
-                "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
-    del acc, micro, emit
+    specs = [("acc", S, torch.float32, 8.0)] + [(f"m{k}", S, torch.int16, 2.0) for k in range(nm)]
+    specs += [("emit", S, torch.int16, 2.0)]
+    v = buffers(specs, seq)
+    for k in range(nm):
+        synth.fill_device(v[f"m{k}"], segs, synth.key(w.name, "micro_grad", 0, k, w.t_first),
+                          *w.micro_grad)
+    record("accum_vec_kernel", "accum1p3b: 162,500,000-element shard, 4 micro-batches "
+           "(overwrite, add, add, add+emit bf16 without fp32 store)", S * (6 + 10 + 10 + 8),
+           timed(lambda: seq(v), reps=5))
+    del v
     torch.cuda.empty_cache()
 
     # the whole no_sync step of accum1p3b: every rank accumulates its 4
     # micro-batches, then the shard step -- the last accumulate as its own
     # call (emit bf16) or folded into the step (zero_shard_step_accumulate)
     hp = z.AdamW(**w.hp)
-    accs = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(w.n_d)]
-    micro = [[torch.empty(S, dtype=torch.int16, device=dev) for _ in range(w.n_micro)]
-             for _ in range(w.n_d)]
-    for q in range(w.n_d):
-        for k in range(w.n_micro):
-            synth.fill_device(micro[q][k], segs, synth.key(w.name, "micro_grad", q, k, w.t_first),
-                              *w.micro_grad)
-    contribs = [torch.empty(S, dtype=torch.int16, device=dev) for _ in range(w.n_d)]
-    state = [torch.zeros(S, dtype=torch.float32, device=dev) for _ in range(3)]
-    pout = torch.empty(L.padded, dtype=torch.int16, device=dev)
-    scale = 1.0 / w.n_micro
 
-    def job(fused):
-        for q in range(w.n_d):
-            for k in range(w.n_micro - (1 if fused else 0)):
-                last = k == w.n_micro - 1
+    def job(v, fused):
+        for q in range(nd):
+            for k in range(nm - (1 if fused else 0)):
+                last = k == nm - 1
                 flags = (z.ACC_OVERWRITE if k == 0 else 0) | (
                     z.ACC_EMIT_BF16 | z.ACC_NO_STORE if last else 0)
-                z.zero_grad_accumulate(accs[q], micro[q][k], scale, flags,
-                                       contribs[q] if last else None)
+                z.zero_grad_accumulate(v[f"a{q}"], v[f"m{q}_{k}"], scale, flags,
+                                       v[f"c{q}"] if last else None)
+        st = (v["master"], v["exp_avg"], v["exp_avg_sq"], v["param_out"])
         if fused:
-            z.zero_shard_step_accumulate(L, hp, w.t_first, accs, [mq[-1] for mq in micro], scale,
-                                         z.DTYPE_BF16, z.GRAD_COMPACT, *state, pout,
-                                         z.OUT_AG_SLOT)
+            z.zero_shard_step_accumulate(L, hp, w.t_first, [v[f"a{q}"] for q in range(nd)],
+                                         [v[f"m{q}_{nm - 1}"] for q in range(nd)], scale,
+                                         z.DTYPE_BF16, z.GRAD_COMPACT, *st, z.OUT_AG_SLOT)
         else:
-            z.zero_shard_step(L, hp, w.t_first, contribs, z.GRAD_COMPACT, *state, pout,
-                              z.OUT_AG_SLOT)
+            z.zero_shard_step(L, hp, w.t_first, [v[f"c{q}"] for q in range(nd)], z.GRAD_COMPACT,
+                              *st, z.OUT_AG_SLOT)
 
-    nd, nm = w.n_d, w.n_micro
+    specs = [(f"a{q}", S, torch.float32, 8.0) for q in range(nd)]
+    specs += [(f"m{q}_{k}", S, torch.int16, 2.0) for q in range(nd) for k in range(nm)]
+    specs += [(f"c{q}", S, torch.int16, 2.0) for q in range(nd)]
+    specs += [(k, S, torch.float32, 8.0) for k in ("master", "exp_avg", "exp_avg_sq")]
+    specs += [("param_out", L.padded, torch.int16, 2.0)]
+    v = buffers(specs, lambda v: job(v, True))
+    for q in range(nd):
+        for k in range(nm):
+            synth.fill_device(v[f"m{q}_{k}"], segs,
+                              synth.key(w.name, "micro_grad", q, k, w.t_first), *w.micro_grad)
     for fused in (False, True):
-        ms = timed(lambda: job(fused), reps=3)
+        ms = timed(lambda: job(v, fused), reps=3)
         if fused:
             nbytes = S * (nd * (6 + 10 * (nm - 2)) + 6 * nd + 26)
             desc = (f"accum1p3b job: {nd} ranks x {nm - 1} accumulate calls, then the step "
@@ -310,11 +342,9 @@ def aux_kernels(z, synth, workloads):
             nbytes = S * (nd * (6 + 10 * (nm - 2) + 8) + 2 * nd + 26)
             desc = (f"accum1p3b job: {nd} ranks x {nm} accumulate calls (last emits bf16), "
                     "then the step")
-        out.append({"kernel": "accum_vec_kernel + step_vec_kernel" + (" (fused)" if fused else ""),
-                    "workload": desc, "bytes_per_call": nbytes, "ms": ms,
-                    "GBps": nbytes / (ms * 1e-3) / 1e9,
-                    "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS})
-    del accs, micro, contribs, state, pout
+        record("accum_vec_kernel + step_vec_kernel" + (" (fused)" if fused else ""), desc,
+               nbytes, ms)
+    del v
     torch.cuda.empty_cache()
     return out
 
@@ -537,7 +567,7 @@ def main():
               flush=True)
         del inp
     torch.cuda.empty_cache()
-    aux = nxt + ([] if args.no_aux else aux_kernels(z, synth, workloads))
+    aux = nxt + ([] if args.no_aux else aux_kernels(z, synth, workloads, args.placement))
     for a in aux:
         print(f"# {a.get('row', a['kernel'])}: {a['ms']:.3f} ms, {a['GBps']:.0f} GB/s "
               f"({100 * a['frac']:.1f} % of 8 TB/s)", file=sys.stderr, flush=True)
@@ -569,6 +599,8 @@ def main():
                      "kernel": step_kernel_name(w.n_d, w.grad_layout == "flat"
                                                 or w.out_mode == "ag_slot"),
                      "kernel_avg_ms": k_avg,
+                     "kernel_median_ms": sorted(kernel_ms)[len(kernel_ms) // 2],
+                     "kernel_min_ms": min(kernel_ms),
                      "algorithmic_bytes_per_launch": alg_bytes, "kernel_hash": kernel_hash()},
         "cpu_baseline": cpu,
         "same_mix_ceiling": {"GBps": ceil_gbps, "frac_of_peak": ceil_gbps / PEAK_HBM_GBPS,
