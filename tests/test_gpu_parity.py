@@ -851,6 +851,68 @@ def test_reshard_gpt2s_state_8_to_4_ranks_round_trip():
         assert_bitwise(back.cpu().numpy(), src_h[r], f"round trip rank {r}")
 
 
+@pytest.mark.timeout(600)
+def test_llama8b_pack_gather_reshard_full_size():
+    """Full-size pack, gather and re-cut on the Llama-3-8B list (8.03e9
+    elements; each call is split over several launches).  Values are keyed
+    by stream position, so the expected value of every position is known:
+    sampled positions are checked against the generator and the oracle's
+    layout, and every position against the concatenated tensors."""
+    w = workloads.get("llama8b")
+    pl = oracle.plan(w.numel, w.cap, 8)
+    L0 = z.Layout(w.numel, w.cap, 8, 0)
+    P, psi = pl.padded_total, sum(w.numel)
+    key = synth.key(w.name, "grad", 0, 0, 1)
+    dist = w.grad
+    rng = np.random.default_rng(5)
+    fpos = np.unique(np.concatenate([rng.integers(0, P, 1 << 18), np.arange(64),
+                                     np.arange(P - 64, P)]))
+    b = np.searchsorted(pl.padded_off, fpos, side="right") - 1
+    off = fpos - pl.padded_off[b]
+    xs = np.where(off < pl.len[b], pl.stream_off[b] + off, -1)
+    expect = synth.values_at(xs, key, *dist, synth.OUT_BF16)
+
+    say("  pack 291 tensors -> 8.03e9-element flat buffer")
+    tens = [torch.empty(n, dtype=torch.int16, device=DEV) for n in w.numel]
+    for t, segs in zip(tens, synth.tensor_segments(w.numel)):
+        synth.fill_device(t, segs, key, *dist)
+    flat = torch.full((P,), CANARY, dtype=torch.int16, device=DEV)
+    z.zero_bucket_pack(L0, tens, flat)
+    torch.cuda.synchronize()
+    assert_bitwise(flat[torch.from_numpy(fpos).to(DEV)].cpu().numpy().view(np.uint16), expect,
+                   "packed flat buffer")
+    stream_all = torch.cat([t.view(-1) for t in tens])
+    del tens
+    torch.cuda.empty_cache()
+
+    say("  gather 8 shards -> flat buffer")
+    shards = []
+    for q in range(8):
+        sh = torch.empty(pl.shard_len, dtype=torch.int16, device=DEV)
+        synth.fill_device(sh, synth.shard_segments(pl.stream_off, pl.len, pl.padded_len,
+                                                   pl.shard_off, 8, q), key, *dist)
+        shards.append(sh)
+    out = torch.full((P,), CANARY, dtype=torch.int16, device=DEV)
+    z.zero_gather_params(L0, shards, out)
+    torch.cuda.synchronize()
+    assert_bitwise(out[torch.from_numpy(fpos).to(DEV)].cpu().numpy().view(np.uint16), expect,
+                   "gathered flat buffer")
+    assert torch.equal(out, flat), "gather and pack disagree"
+    del out, flat
+    torch.cuda.empty_cache()
+
+    say("  re-cut the 8 bf16 shards for one rank (the whole stream in order)")
+    L1 = z.Layout(w.numel, w.cap, 1, 0)
+    assert L1.shard == psi
+    dst = torch.full((psi,), CANARY, dtype=torch.int16, device=DEV)
+    z.zero_reshard(L0, shards, L1, dst)
+    torch.cuda.synchronize()
+    xs1 = np.unique(rng.integers(0, psi, 1 << 18))
+    assert_bitwise(dst[torch.from_numpy(xs1).to(DEV)].cpu().numpy().view(np.uint16),
+                   synth.values_at(xs1, key, *dist, synth.OUT_BF16), "re-cut shard")
+    assert torch.equal(dst, stream_all), "re-cut shard differs from the tensors in stream order"
+
+
 # ------------------------------------------------------------------ FSDP2 per-parameter layout
 def test_gpt2s_fsdp2_steps_full():
     """GPT-2-small list sharded per parameter along dim 0 over 8 ranks (the
