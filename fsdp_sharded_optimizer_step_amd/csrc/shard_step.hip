@@ -428,19 +428,26 @@ int cu_count() {
   return n;
 }
 
-constexpr int kDefaultThreads = 256;
-
-// Launch policy, from measurements on MI355X: a read-dominated step (64 or
-// more bytes of contributions per element) streams best with non-temporal
-// accesses and one 256-thread block per CU; a step with a larger write share
-// (small N_d) with ordinary accesses and two blocks per CU.
+// Launch policy, from measurements on MI355X (Llama-3-8B shard, N_d = 8,
+// buffers placed by zero_placement_plan):
+//   read-dominated (64 or more bytes of contributions per element):
+//     non-temporal accesses, one 256-thread block per CU;
+//   bf16 contributions otherwise: ordinary accesses, two 128-thread blocks
+//     per CU (7.00 ms against 7.07 with two 256-thread blocks);
+//   fp32 contributions: ordinary accesses, two 256-thread blocks per CU;
+//   accumulator + last micro-batch: ordinary accesses, one 256-thread block
+//     per CU (12.6 ms against 13.2 with two).
 constexpr bool read_dominated(int nd, int gt) { return nd * contrib_bytes(gt) >= 64; }
-int default_blocks_per_cu(int nd, int gt) {
+struct Policy {
+  int blocks_per_cu, threads;
+};
+Policy default_policy(int nd, int gt) {
+  if (read_dominated(nd, gt)) return Policy{1, 256};
   switch (gt) {
-    case GT_F32: return read_dominated(nd, GT_F32) ? 1 : 2;
+    case GT_F32: return Policy{2, 256};
     case GT_ACC_BF16:
-    case GT_ACC_F32: return read_dominated(nd, GT_ACC_BF16) ? 1 : 2;
-    default: return read_dominated(nd, GT_BF16) ? 1 : 2;
+    case GT_ACC_F32: return Policy{1, 256};
+    default: return Policy{2, 128};
   }
 }
 
@@ -554,7 +561,7 @@ Scalars make_scalars(const zero_adamw& hp, int64_t t) {
 }
 
 struct LaunchShape {
-  int threads = kDefaultThreads, blocks_cap = 0, path = 0;
+  int threads = 0, blocks_cap = 0, path = 0;  // 0: the policy's choice
 };
 
 int parse_options(const zero_step_options* opt, LaunchShape& ls) {
@@ -602,8 +609,9 @@ int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int3
   bool aligned = aligned16(c.master) && aligned16(c.m) && aligned16(c.v) && aligned16(c.pout) &&
                  (!c.gout || aligned16(c.gout));
   for (int q = 0; q < n_ins; ++q) aligned = aligned && aligned16(ins[q]);
-  const int threads = ls.threads;
-  const int cap = ls.blocks_cap > 0 ? ls.blocks_cap : cu_count() * default_blocks_per_cu(nd, c.gt);
+  const Policy pol = default_policy(nd, c.gt);
+  const int threads = ls.threads > 0 ? ls.threads : pol.threads;
+  const int cap = ls.blocks_cap > 0 ? ls.blocks_cap : cu_count() * pol.blocks_per_cu;
   const bool allow_vec = ls.path == 0 && aligned;
   const int64_t r = L->rank;
 
