@@ -340,17 +340,23 @@ __global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND, GT> A) 
 // search over the tile prefix sums, so a 38.6M-element embedding and
 // 96-element norm slices share one launch without idle blocks.  Regions whose
 // addresses are not all 16-byte aligned (bit clear in `vec`) run element by
-// element.
-constexpr int kTableMax = 32;
-struct Table {
-  int64_t i0[kTableMax], f0[kTableMax], n[kTableMax];
-  int64_t tile0[kTableMax + 1];  // first tile of each region; tile0[count] = total
-  uint32_t vec;
+// element.  A launch takes up to 64 regions for the compile-time rank counts
+// and 32 for the runtime-N_d instantiation, whose pointer arrays are larger:
+// the kernel arguments stay under 4 KB.
+template <int CAP>
+struct TableT {
+  int64_t i0[CAP], f0[CAP], n[CAP];
+  int64_t tile0[CAP + 1];  // first tile of each region; tile0[count] = total
+  uint64_t vec;
   int32_t count;
 };
+template <int ND>
+using TableFor = TableT<(ND > 0 ? 64 : 32)>;
+using HostTable = TableT<64>;
 
 template <int ND, int GROUP, bool NT, int GT>
-__global__ void __launch_bounds__(256) step_table_kernel(const ArgsFor<ND, GT> A, const Table T) {
+__global__ void __launch_bounds__(256) step_table_kernel(const ArgsFor<ND, GT> A,
+                                                         const TableFor<ND> T) {
   const int64_t span = (int64_t)blockDim.x << 3;
   const int64_t total = T.tile0[T.count];
   for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
@@ -365,7 +371,7 @@ __global__ void __launch_bounds__(256) step_table_kernel(const ArgsFor<ND, GT> A
     if (e0 >= n) continue;
     const int64_t i = T.i0[lo] + e0, f = T.f0[lo] + e0;
     const int64_t gi = A.flat_grad ? f : i, oi = A.slot_out ? f : i;
-    if (((T.vec >> lo) & 1u) && e0 + 8 <= n) {
+    if (((T.vec >> lo) & 1ull) && e0 + 8 <= n) {
       step8<ND, GROUP, NT, GT>(A, i, gi, oi);
     } else {
       const int64_t m = n - e0 < 8 ? n - e0 : 8;
@@ -456,9 +462,12 @@ Policy default_policy(int nd, int gt) {
 enum : int { K_PLAIN = 0, K_MAP = 1, K_TABLE = 2 };
 struct Work {
   const Region* reg;
-  const Table* tab;
+  const HostTable* tab;
   int blocks, threads;
 };
+
+bool static_nd(int nd) { return nd == 2 || nd == 4 || nd == 8 || nd == 16 || nd == 32 || nd == 64; }
+int table_cap(int nd) { return static_nd(nd) ? 64 : 32; }
 
 template <int ND, int GT, int KIND, bool NT>
 int launch_nt(const Call& c, const Work& w, hipStream_t s) {
@@ -468,12 +477,26 @@ int launch_nt(const Call& c, const Work& w, hipStream_t s) {
   // loads, which would otherwise spill at N_d = 64)
   constexpr int GMAX = fused(GT) ? 8 : 16;
   constexpr int GROUP = ND > GMAX ? GMAX : (ND > 1 ? ND - 1 : 1);
-  if constexpr (KIND == K_TABLE)
+  if constexpr (KIND == K_TABLE) {
+    using Tab = TableFor<ND>;
+    static_assert(sizeof(ArgsFor<ND, GT>) + sizeof(Tab) <= 4096, "kernel arguments");
+    Tab T;
+    const int n = w.tab->count;
+    for (int k = 0; k < n; ++k) {
+      T.i0[k] = w.tab->i0[k];
+      T.f0[k] = w.tab->f0[k];
+      T.n[k] = w.tab->n[k];
+      T.tile0[k] = w.tab->tile0[k];
+    }
+    T.tile0[n] = w.tab->tile0[n];
+    T.vec = w.tab->vec;
+    T.count = n;
     hipLaunchKernelGGL((step_table_kernel<ND, GROUP, NT, GT>), dim3(w.blocks), dim3(w.threads), 0,
-                       s, A, *w.tab);
-  else
+                       s, A, T);
+  } else {
     hipLaunchKernelGGL((step_vec_kernel<ND, KIND == K_MAP, GROUP, NT, GT>), dim3(w.blocks),
                        dim3(w.threads), 0, s, A);
+  }
   return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
 }
 
@@ -617,9 +640,10 @@ int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int3
 
   if (map && !L->fixed()) {
     // per-parameter (dim-0) layout: every tensor is its own bucket; the
-    // non-empty slices go to table launches of up to kTableMax regions
+    // non-empty slices go to table launches of up to table_cap(nd) regions
     const int64_t span_e = (int64_t)threads * 8;
-    Table T;
+    const int tcap = table_cap(nd);
+    HostTable T;
     T.count = 0;
     T.vec = 0;
     T.tile0[0] = 0;
@@ -641,10 +665,10 @@ int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int3
       T.i0[k] = i0;
       T.f0[k] = f0;
       T.n[k] = sl;
-      if (allow_vec && i0 % 8 == 0 && f0 % 8 == 0) T.vec |= 1u << k;
+      if (allow_vec && i0 % 8 == 0 && f0 % 8 == 0) T.vec |= 1ull << k;
       T.tile0[k + 1] = T.tile0[k] + (sl + span_e - 1) / span_e;
       T.count = k + 1;
-      if (T.count == kTableMax) {
+      if (T.count == tcap) {
         const int rc = flush();
         if (rc != ZERO_OK) return rc;
         T.tile0[0] = 0;

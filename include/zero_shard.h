@@ -20,7 +20,9 @@
  * the library performs the local arithmetic of the Reduce-Scatter (a sum in
  * fixed rank order, then the division by N_d), the optimizer step and the
  * local write of the All-Gather (the rank's bf16 slice into its slot of the
- * gathered buffer), in one kernel per call.  No collective is issued.
+ * gathered buffer), in one streaming pass over the shard (one kernel launch
+ * per call for a bucketed layout with 16-byte aligned buffers; per-parameter
+ * layouts take one launch per 32 tensors).  No collective is issued.
  *
  * Conventions for every entry point:
  *   - Returns ZERO_OK or a negative zero_status.  Arguments are validated on
@@ -228,7 +230,8 @@ int zero_shard_step(const zero_layout* layout, const zero_adamw* hp, int64_t t,
  *   a = G_0; a = a + G_q for q = 1..n_d-1, then the same update.  Reads
  *   4*n_d + 26 bytes per shard element instead of 2*n_d + 26.
  * blocks <= 0 and threads <= 0 pick the defaults; threads must be a multiple
- * of 64 and at most 256; path 0 = automatic, 1 = force the scalar kernel.
+ * of 64 and at most 256; path 0 = automatic, 1 = force element-by-element
+ * (scalar) processing.
  * opt == NULL means {ZERO_DTYPE_BF16, 0, 0, 0}.  Results do not depend on
  * blocks, threads or path.  Errors as for zero_shard_step, plus ZERO_EINVAL
  * for a bad dtype or launch shape. */

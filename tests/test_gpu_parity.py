@@ -938,6 +938,9 @@ DIM0_EDGE = [
      4, 3, "flat", "ag_slot"),
     ([((k * 7) % 41 + 1, (k * 5) % 13 + 1) if k % 9 else (64, 64) for k in range(75)],
      8, 0, "compact", "ag_slot"),
+    # runtime rank count: table launches of 32 slices
+    ([((k * 7) % 41 + 1, (k * 5) % 13 + 1) if k % 9 else (64, 64) for k in range(75)],
+     3, 2, "flat", "ag_slot"),
 ]
 
 
