@@ -559,6 +559,9 @@ def main():
     ceil_gbps, ceil_cfg = measure.stream_ceiling(inp.grads, inp.state, inp.pout, S)
     print(f"# same-mix streaming ceiling: {ceil_gbps:.0f} GB/s {ceil_cfg}", file=sys.stderr,
           flush=True)
+    probes = measure.stream_probes(inp.grads, inp.state, inp.pout, S)
+    print(f"# pure read {probes['read']['GBps']:.0f} GB/s, copy {probes['copy']['GBps']:.0f} GB/s "
+          "on the same buffers", file=sys.stderr, flush=True)
     nxt = []
     tuning = None
     if inp.pool is not None:
@@ -623,7 +626,8 @@ def main():
         "same_mix_ceiling": {"GBps": ceil_gbps, "frac_of_peak": ceil_gbps / PEAK_HBM_GBPS,
                              "step_frac_of_ceiling": achieved / ceil_gbps,
                              "kernel": "measure/stream_ceiling.hip: the step's bytes, "
-                                       "trivial arithmetic", "best_config": ceil_cfg},
+                                       "trivial arithmetic", "best_config": ceil_cfg,
+                             "pure_read": probes["read"], "copy": probes["copy"]},
         "placement_comparison": other,
         "aux_kernels": aux,
     }

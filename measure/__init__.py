@@ -19,6 +19,10 @@ def _load():
                                               C.POINTER(C.c_void_p), C.c_void_p, C.c_int64,
                                               C.c_int32, C.c_int32, C.c_void_p]
         lib.stream_ceiling_launch.restype = C.c_int
+        lib.stream_probe_launch.argtypes = [C.c_int32, C.POINTER(C.c_void_p), C.c_int32,
+                                            C.POINTER(C.c_void_p), C.c_void_p, C.c_int64,
+                                            C.c_int32, C.c_int32, C.c_void_p]
+        lib.stream_probe_launch.restype = C.c_int
         _lib = lib
     return _lib
 
@@ -52,3 +56,39 @@ def stream_ceiling(grads, state, out, n: int, reps: int = 5):
             if gbps > best[0]:
                 best = (gbps, {"blocks_per_cu": bpc, "nontemporal": bool(nt), "ms": ms})
     return best
+
+
+def stream_probes(grads, state, out, n: int, reps: int = 5):
+    """Pure-read and copy bandwidth (GB/s) on the given (scratch) buffers:
+    the read of every byte the step reads (2*N_d + 12 per element), and a copy
+    of state array 0 into state array 1 (8 bytes per element); best over a
+    few launch shapes.  Overwrites state array 1 and `out`."""
+    import torch
+    lib = _load()
+    nd = len(grads)
+    g = (C.c_void_p * nd)(*[t.data_ptr() for t in grads])
+    s = (C.c_void_p * 3)(*[t.data_ptr() for t in state])
+    n = n // 8 * 8
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    res = {}
+    for kind, name, bpe in ((0, "read", 2 * nd + 12), (1, "copy", 8)):
+        best = (0.0, None)
+        for bpc in (1, 2, 4, 8):
+            for nt in (0, 1):
+                args = (kind, g, nd, s, out.data_ptr(), n, cus * bpc, nt, stream.cuda_stream)
+                if lib.stream_probe_launch(*args) != 0:
+                    raise RuntimeError("stream_probe_launch failed")
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    lib.stream_probe_launch(*args)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / reps
+                gbps = n * bpe / (ms * 1e-3) / 1e9
+                if gbps > best[0]:
+                    best = (gbps, {"blocks_per_cu": bpc, "nontemporal": bool(nt), "ms": ms})
+        res[name] = {"GBps": best[0], "config": best[1]}
+    return res

@@ -59,6 +59,30 @@ __global__ void __launch_bounds__(256) mix_kernel(const MixArgs a) {
   }
 }
 
+// Pure-read stream over the same buffers (every contribution and state
+// array read once); one 16-byte store per lane at the end keeps the loads.
+template <bool NT>
+__global__ void __launch_bounds__(256) read_kernel(const MixArgs a) {
+  const int64_t T = (int64_t)gridDim.x * blockDim.x;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int64_t v = tid; v < a.nvec; v += T) {
+    for (int q = 0; q < a.nd; ++q) acc ^= ld<NT>(a.g[q] + v);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) acc += ld<NT>(a.s[k] + 2 * v) ^ ld<NT>(a.s[k] + 2 * v + 1);
+  }
+  if (tid < a.nvec) st<NT>(a.p + tid, acc);
+}
+
+// Plain copy of state array 0 into state array 1 (read 4, write 4 bytes per
+// element).
+template <bool NT>
+__global__ void __launch_bounds__(256) copy_kernel(const MixArgs a) {
+  const int64_t T = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < 2 * a.nvec; v += T)
+    st<NT>(a.s[1] + v, ld<NT>(a.s[0] + v));
+}
+
 }  // namespace
 
 extern "C" {
@@ -91,6 +115,34 @@ int stream_ceiling_launch(const void* const* grads, int32_t nd, void* const* sta
   } else {
     if (nt) hipLaunchKernelGGL((mix_kernel<0, true>), dim3(blocks), dim3(256), 0, stream, a);
     else hipLaunchKernelGGL((mix_kernel<0, false>), dim3(blocks), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// kind 0: pure read of every buffer the step reads; kind 1: copy of state
+// array 0 into state array 1.  Arguments as for stream_ceiling_launch.
+int stream_probe_launch(int32_t kind, const void* const* grads, int32_t nd, void* const* state,
+                        void* out, int64_t n, int32_t blocks, int32_t nt, hipStream_t stream) {
+  if (kind < 0 || kind > 1 || nd < 1 || nd > kMaxRanks || n < 0 || n % 8 != 0 || blocks < 1 ||
+      !grads || !state || !out)
+    return -1;
+  MixArgs a;
+  for (int q = 0; q < kMaxRanks; ++q) a.g[q] = q < nd ? (const u32x4*)grads[q] : nullptr;
+  for (int k = 0; k < 3; ++k) a.s[k] = (u32x4*)state[k];
+  a.p = (u32x4*)out;
+  a.nvec = n / 8;
+  a.nd = nd;
+  for (int q = 0; q < nd; ++q)
+    if (!grads[q] || ((uintptr_t)grads[q] & 15u)) return -1;
+  for (int k = 0; k < 3; ++k)
+    if (!state[k] || ((uintptr_t)state[k] & 15u)) return -1;
+  if ((uintptr_t)out & 15u) return -1;
+  if (kind == 0) {
+    if (nt) hipLaunchKernelGGL((read_kernel<true>), dim3(blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((read_kernel<false>), dim3(blocks), dim3(256), 0, stream, a);
+  } else {
+    if (nt) hipLaunchKernelGGL((copy_kernel<true>), dim3(blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((copy_kernel<false>), dim3(blocks), dim3(256), 0, stream, a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }
