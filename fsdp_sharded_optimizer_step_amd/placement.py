@@ -7,12 +7,13 @@ here, and results do not depend on the placement.
 """
 from __future__ import annotations
 
-from .binding import GRAD_FLAT, OUT_AG_SLOT, zero_placement_plan
+from .binding import GRAD_FLAT, OUT_AG_SLOT, zero_placement_plan, zero_shard_step
 
 GiB = 1 << 30
 LANE_BYTES = 32 * GiB   # MI355X, measured: lanes 32 GiB apart ...
 N_LANES = 3             # ... three of them (a 96 GiB period)
 ALIGN = 2 << 20
+SLACK = 32 * GiB        # spare room measured to avoid the slow placements
 
 
 class Pool:
@@ -59,6 +60,15 @@ class Pool:
     def __getitem__(self, name):
         return self.views[name]
 
+    @property
+    def grads(self):
+        """The contribution views g0, g1, ... in rank order."""
+        out, q = [], 0
+        while f"g{q}" in self.views:
+            out.append(self.views[f"g{q}"])
+            q += 1
+        return out
+
 
 def step_specs(layout, grad_dtype=None, grad_layout: int = 0, out_mode: int = OUT_AG_SLOT,
                reduced_grad: bool = False, accumulators: bool = False):
@@ -87,3 +97,35 @@ def step_pool(layout, device="cuda:0", lane_bytes=LANE_BYTES, n_lanes=N_LANES, a
     """A Pool holding step_specs(layout, **spec_kw)."""
     return Pool(step_specs(layout, **spec_kw), device=device, lane_bytes=lane_bytes,
                 n_lanes=n_lanes, align=align, slack=slack, choose=choose, shift_step=shift_step)
+
+
+def step_timer(layout, hp, t: int, grad_layout: int, out_mode: int, reps: int = 4):
+    """A `choose` callback: views -> milliseconds of one zero_shard_step on
+    them (HIP events on the current stream, after one untimed call)."""
+    import torch
+
+    def ms(v):
+        g = [v[f"g{q}"] for q in range(layout.n_d)]
+        args = (layout, hp, t, g, grad_layout, v["master"], v["exp_avg"], v["exp_avg_sq"],
+                v["param_out"], out_mode)
+        zero_shard_step(*args)
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            zero_shard_step(*args)
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    return ms
+
+
+def tuned_step_pool(layout, hp, t: int, grad_layout: int = 0, out_mode: int = OUT_AG_SLOT,
+                    slack=SLACK, device="cuda:0", **spec_kw) -> Pool:
+    """step_pool with `slack` spare bytes, its start chosen by timing the
+    step at 4 GiB shifts (the buffers' contents are arbitrary afterwards)."""
+    return step_pool(layout, device=device, slack=slack, grad_layout=grad_layout,
+                     out_mode=out_mode,
+                     choose=step_timer(layout, hp, t, grad_layout, out_mode), **spec_kw)

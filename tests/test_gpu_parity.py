@@ -256,6 +256,17 @@ def test_planned_placement_gives_identical_results(gl, om):
         assert torch.equal(pool[name].cpu(), t.cpu()), name
 
 
+def test_tuned_step_pool_times_the_step_at_each_shift():
+    from fsdp_sharded_optimizer_step_amd import placement as zp
+    L = z.Layout([300_001, 77], 65_536, 8, 5)
+    pool = zp.tuned_step_pool(L, z.AdamW(), 1, z.GRAD_COMPACT, z.OUT_SHARD, slack=2 << 20,
+                              lane_bytes=1 << 20, align=256, shift_step=1 << 20)
+    assert [sh for sh, _ in pool.tuning] == [0, 1 << 20, 2 << 20]
+    assert all(ms > 0 for _, ms in pool.tuning)
+    assert pool.shift == min(pool.tuning, key=lambda x: x[1])[0]
+    assert len(pool.grads) == 8 and pool["param_out"].numel() == L.shard
+
+
 def test_empty_shard_is_a_no_op():
     L = z.Layout([], 0, 4, 0)
     e = torch.empty(0, dtype=torch.float32, device=DEV)
@@ -1101,4 +1112,83 @@ def test_hip_graph_capture_of_accumulate_and_step():
         got = [x.cpu().numpy() for x in graphed["state"]] + [u16(graphed["pout"])]
         for a, b in zip(got, expected[r]):
             assert_bitwise(a, b, f"graph replay {r}")
+        del junk
+
+
+def test_hip_graph_capture_of_pack_fused_step_table_step_gather_and_reshard():
+    """Every other entry point that launches kernels is capturable too: bucket
+    pack (FLAT contributions), the step with the last micro-batch folded in,
+    a per-parameter (table) step, the parameter gather and a re-cut, captured
+    in one HIP graph; each of several replays equals the same sequence run
+    eagerly, bit for bit."""
+    shapes = [((k * 7) % 41 + 1, (k * 5) % 13 + 1) if k % 9 else (64, 64) for k in range(40)]
+    numel = [int(np.prod(s)) for s in shapes]
+    rows = [s[0] for s in shapes]
+    n_d, rank, t = 4, 1, 5
+    Lb = z.Layout(numel, 1000, n_d, rank)                 # bucketed, FLAT contributions
+    Ld = z.Layout(numel, 0, n_d, rank, rows=rows)         # per-parameter
+    L2 = z.Layout(numel, 1000, 2, 0)                      # re-cut target
+    hp = z.AdamW()
+    rng = np.random.default_rng(77)
+
+    def bf16(n, scale=1e-3):
+        return torch.from_numpy(oracle.round_bf16((rng.standard_normal(n) * scale)
+                                                  .astype(np.float32)).view(np.int16)).to(DEV)
+
+    def f32(n, scale=1e-3):
+        return torch.from_numpy((rng.standard_normal(n) * scale).astype(np.float32)).to(DEV)
+
+    tens = [[bf16(n) for n in numel] for _ in range(n_d)]
+    accs = [f32(Ld.shard) for _ in range(n_d)]
+    micro = [bf16(Ld.shard, 2e-3) for _ in range(n_d)]
+    shards = [bf16(Lb.shard, 0.02) for _ in range(n_d)]
+    init = [f32(Lb.shard, 0.02), f32(Lb.shard, 1e-4), f32(Lb.shard, 1e-6).abs(),
+            f32(Ld.shard, 0.02), f32(Ld.shard, 1e-4), f32(Ld.shard, 1e-6).abs()]
+
+    def make_bufs():
+        return dict(flat=[torch.zeros(Lb.padded, dtype=torch.int16, device=DEV)
+                          for _ in range(n_d)],
+                    state=[x.clone() for x in init],
+                    pout_b=torch.full((Lb.padded,), CANARY, dtype=torch.int16, device=DEV),
+                    pout_d=torch.full((Ld.padded,), CANARY, dtype=torch.int16, device=DEV),
+                    full=torch.zeros(Lb.padded, dtype=torch.int16, device=DEV),
+                    recut=torch.zeros(L2.shard, dtype=torch.float32, device=DEV))
+
+    def sequence(b, stream=None):
+        for q in range(n_d):
+            z.zero_bucket_pack(Lb, tens[q], b["flat"][q], stream=stream)
+        z.zero_shard_step(Lb, hp, t, b["flat"], z.GRAD_FLAT, *b["state"][:3], b["pout_b"],
+                          z.OUT_AG_SLOT, stream=stream)
+        z.zero_shard_step_accumulate(Ld, hp, t, accs, micro, 0.25, z.DTYPE_BF16, z.GRAD_COMPACT,
+                                     *b["state"][3:], b["pout_d"], z.OUT_AG_SLOT, stream=stream)
+        z.zero_gather_params(Lb, shards, b["full"], stream=stream)
+        z.zero_reshard(Lb, [b["state"][0]] * n_d, L2, b["recut"], stream=stream)
+
+    def snapshot(b):
+        return ([u16(x) for x in b["flat"]] + [x.cpu().numpy() for x in b["state"]] +
+                [u16(b["pout_b"]), u16(b["pout_d"]), u16(b["full"]), b["recut"].cpu().numpy()])
+
+    eager = make_bufs()
+    expected = []
+    for _ in range(3):
+        sequence(eager)
+        torch.cuda.synchronize()
+        expected.append(snapshot(eager))
+
+    graphed = make_bufs()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            sequence(graphed, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        junk = torch.ones(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(snapshot(graphed), expected[r])):
+            assert_bitwise(a, b, f"graph replay {r}, buffer {k}")
         del junk
