@@ -400,6 +400,69 @@ def test_nonfinite_gradients_propagate_elementwise():
     assert_bitwise(u16(p)[ok], ep[ok], "finite params")
 
 
+@pytest.mark.parametrize("contrib", ["bf16", "f32", "fused"])
+def test_subnormals_are_kept_bitwise(contrib):
+    """Subnormal contributions, moments, master weights and sums: the kernels
+    keep IEEE subnormals (no flush to zero), as the oracle does; every output
+    is compared bit for bit, three steps (t = 1 makes v' = C2*g*g subnormal)."""
+    n_d, S = 8, 8192
+    rng = np.random.default_rng(21)
+
+    def sub32(n, lo=1, hi=0x007FFFFF):     # positive and negative binary32 subnormals
+        b = rng.integers(lo, hi, n).astype(np.uint32) | (rng.integers(0, 2, n).astype(np.uint32) << 31)
+        return b.view(np.float32)
+
+    def mix32(n, scale):
+        x = (rng.standard_normal(n) * scale).astype(np.float32)
+        k = rng.random(n) < 0.5
+        x[k] = sub32(int(k.sum()))
+        return x
+
+    L = z.Layout([S * n_d], 0, n_d, 3)
+    th, m, v = mix32(S, 1e-38), mix32(S, 1e-38), np.abs(mix32(S, 1e-39))
+    dev_state = [torch.from_numpy(a.copy()).to(DEV) for a in (th, m, v)]
+    o_state = [a.copy() for a in (th, m, v)]
+    p = torch.empty(S, dtype=torch.int16, device=DEV)
+    gout = torch.empty(S, dtype=torch.float32, device=DEV)
+    hp_z, hp_o = z.AdamW(lr=1e-38, eps=1e-40), oracle.AdamW(lr=1e-38, eps=1e-40)
+    for t in (1, 2, 3):
+        if contrib == "bf16":
+            # bf16 subnormal patterns 0x0001..0x007F (and negatives), some normals
+            gh = [np.where(rng.random(S) < 0.7, rng.integers(1, 0x80, S),
+                           rng.integers(0x0080, 0x0400, S)).astype(np.uint16)
+                  | (rng.integers(0, 2, S).astype(np.uint16) << 15) for _ in range(n_d)]
+            z.zero_shard_step(L, hp_z, t, [torch.from_numpy(g.view(np.int16)).to(DEV)
+                                           for g in gh], z.GRAD_COMPACT, *dev_state, p,
+                              z.OUT_SHARD, gout)
+            ep, eg = oracle.shard_step(gh, *o_state, hp_o, t, want_grad=True)
+        else:
+            acc = [mix32(S, 1e-38) for _ in range(n_d)]
+            if contrib == "f32":
+                z.zero_shard_step(L, hp_z, t, [torch.from_numpy(a).to(DEV) for a in acc],
+                                  z.GRAD_COMPACT, *dev_state, p, z.OUT_SHARD, gout)
+                ep, eg = oracle.shard_step_f32(acc, *o_state, hp_o, t, want_grad=True)
+            else:
+                mic = [(rng.integers(1, 0x80, S).astype(np.uint16)
+                        | (rng.integers(0, 2, S).astype(np.uint16) << 15)) for _ in range(n_d)]
+                z.zero_shard_step_accumulate(
+                    L, hp_z, t, [torch.from_numpy(a).to(DEV) for a in acc],
+                    [torch.from_numpy(g.view(np.int16)).to(DEV) for g in mic], 0.25,
+                    z.DTYPE_BF16, z.GRAD_COMPACT, *dev_state, p, z.OUT_SHARD, gout)
+                contribs = [oracle.accumulate(a.copy(), g, 0.25, overwrite=False,
+                                              store_acc=False, emit=True)
+                            for a, g in zip(acc, mic)]
+                ep, eg = oracle.shard_step(contribs, *o_state, hp_o, t, want_grad=True)
+        torch.cuda.synchronize()
+        assert_bitwise(gout.cpu().numpy(), eg, f"{contrib} t={t} reduced gradient")
+        for a, b, what in zip(dev_state, o_state, ("master", "m", "v")):
+            assert_bitwise(a.cpu().numpy(), b, f"{contrib} t={t} {what}")
+        assert_bitwise(u16(p), ep, f"{contrib} t={t} param")
+    # the test is only meaningful if subnormals actually occurred
+    for x in (eg, o_state[1], o_state[2]):
+        x = np.asarray(x)
+        assert ((x != 0) & (np.abs(x) < np.float32(1.1754944e-38))).any()
+
+
 def test_repeat_calls_are_deterministic():
     outs = []
     for _ in range(2):
