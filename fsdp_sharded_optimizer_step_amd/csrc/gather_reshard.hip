@@ -12,8 +12,8 @@
 // checkpoint holds every rank's shards of the parameters and optimizer
 // state, and loading it into a run with a different number of GPUs re-cuts
 // the shards to the new layout.  zero_reshard performs that re-cut for one
-// state array: from the N_d shards of one bucketed layout to one rank's
-// shard of another layout of the same tensor list.
+// state array: from the N_d shards of one layout (bucketed or per-parameter)
+// to one rank's shard of another layout of the same tensor list.
 //
 // Both are copies: gather moves 4 bytes per flat element, reshard 2 x the
 // element size per destination element (2 for bf16, 4 for fp32), plus the
@@ -53,8 +53,9 @@ __device__ __forceinline__ int64_t real_len(const Geo& g, int64_t b) {
 }
 
 // ------------------------------------------------------------------ gather
-// A launch covers a run of buckets with one slice length.  The copy is cut
-// into (bucket, rank, tile) work items, one per block: the block finds its
+// A run of buckets with one slice length is cut into (bucket, rank, tile)
+// work items, one per block, over as many launches of at most kMaxBlocks
+// blocks as it needs: the block finds its
 // item with a few uniform integer divisions and then copies a contiguous
 // tile of the rank's slice into the bucket's slot q -- no per-element index
 // arithmetic.
@@ -235,7 +236,7 @@ int zero_gather_params(const zero_layout* L, const uint16_t* const* rank_shards,
     if (overlap(rank_shards[q], 2 * L->S, full_out, 2 * L->P)) return ZERO_EOVERLAP;
   }
   if (bucket_begin == bucket_end) return ZERO_OK;
-  // One launch per run of buckets with equal slices: the full buckets of a
+  // One `launch` per run of buckets with equal slices: the full buckets of a
   // bucketed layout, its last bucket, or one tensor of a per-parameter layout.
   auto launch = [&](int64_t b0, int64_t nbk, int64_t slice, int64_t sstride,
                     int64_t pstride) -> int {
@@ -296,7 +297,7 @@ int zero_reshard(const zero_layout* src, const void* const* src_shards, const ze
   }
   if (dst->S == 0) return ZERO_OK;
 
-  // One launch: destination range [i0, i0+n) read through geometry gd
+  // One `launch`: destination range [i0, i0+n) read through geometry gd
   // (origin d_base_i / d_base_x), source through gs with its pointers
   // shifted by s_shift elements and stream origin s_base_x.
   auto launch = [&](const Geo& gd, int64_t i0, int64_t n, int64_t d_base_i, int64_t d_base_x,
