@@ -100,6 +100,51 @@ __global__ void __launch_bounds__(kGatherThreads) gather_kernel(const GatherArgs
   }
 }
 
+// Per-parameter layouts: every tensor is its own bucket with its own slice
+// length, so up to kGatherTab tensors share a launch through a table in the
+// kernel arguments (first item, tiles per slice, offsets); a block finds its
+// tensor by binary search over the first items, then (rank, tile) as above.
+constexpr int kGatherTab = 48;
+struct GatherTabArgs {
+  const uint16_t* shard[ZERO_MAX_ND];  // each rank's shard
+  uint16_t* out;                       // flat buffer
+  int64_t shard_off[kGatherTab], flat_off[kGatherTab], slice[kGatherTab];
+  uint32_t tiles[kGatherTab];
+  uint32_t item0[kGatherTab + 1];      // first item of each tensor; item0[n] = total
+  uint64_t vec;                        // bit k: tensor k takes 16-byte copies
+  uint32_t item_base;                  // first item of this launch
+  int32_t n, n_d;
+};
+static_assert(sizeof(GatherTabArgs) <= 4096, "kernel arguments");
+
+__global__ void __launch_bounds__(kGatherThreads) gather_table_kernel(const GatherTabArgs A) {
+  const uint32_t item = A.item_base + blockIdx.x;
+  int lo = 0, hi = A.n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (A.item0[mid] <= item) lo = mid;
+    else hi = mid;
+  }
+  const uint32_t local = item - A.item0[lo];
+  const uint32_t tiles = A.tiles[lo];
+  const uint32_t q = local / tiles;
+  const uint32_t c = local - q * tiles;
+  const int64_t slice = A.slice[lo];
+  const uint16_t* src = A.shard[q] + A.shard_off[lo];
+  uint16_t* dst = A.out + A.flat_off[lo] + (int64_t)q * slice;
+  const int64_t e0 = (int64_t)c * kGatherTile;
+  const int64_t e1 = e0 + kGatherTile < slice ? e0 + kGatherTile : slice;
+  if ((A.vec >> lo) & 1ull) {
+    const u32x4* sv = (const u32x4*)(src + e0);
+    u32x4* dv = (u32x4*)(dst + e0);
+    const int64_t nv = (e1 - e0) >> 3;
+    for (int64_t v = threadIdx.x; v < nv; v += kGatherThreads)
+      st_stream<true>(dv + v, ld_stream<true>(sv + v));
+  } else {
+    for (int64_t e = e0 + threadIdx.x; e < e1; e += kGatherThreads) dst[e] = src[e];
+  }
+}
+
 // ------------------------------------------------------------------ reshard
 // One launch covers the destination shard indices [i0, i0 + n).  The
 // destination index i maps, through geometry gd taken at origin d_base_i,
@@ -277,12 +322,48 @@ int zero_gather_params(const zero_layout* L, const uint16_t* const* rank_shards,
       rc = launch(last, 1, L->s_last, L->s_last, L->p_last);
     return rc;
   }
+  // per-parameter layout: tables of up to kGatherTab non-empty tensors
+  GatherTabArgs T;
+  for (int q = 0; q < ZERO_MAX_ND; ++q) T.shard[q] = q < nd ? rank_shards[q] : nullptr;
+  T.out = full_out;
+  T.n_d = nd;
+  bool base_vec = a16(full_out);
+  for (int32_t q = 0; q < nd; ++q) base_vec = base_vec && a16(rank_shards[q]);
+  T.n = 0;
+  T.vec = 0;
+  T.item0[0] = 0;
+  auto flush = [&]() -> int {
+    const int64_t items = T.item0[T.n];
+    for (int64_t i0 = 0; i0 < items; i0 += kMaxBlocks) {
+      T.item_base = (uint32_t)i0;
+      const unsigned grid = (unsigned)std::min(kMaxBlocks, items - i0);
+      hipLaunchKernelGGL(gather_table_kernel, dim3(grid), dim3(kGatherThreads), 0, stream, T);
+      if (hipGetLastError() != hipSuccess) return ZERO_EHIP;
+    }
+    T.n = 0;
+    T.vec = 0;
+    T.item0[0] = 0;
+    return ZERO_OK;
+  };
   for (int64_t b = bucket_begin; b < bucket_end; ++b) {
     const int64_t sl = L->bucket_slice(b);
-    const int rc = launch(b, 1, sl, sl, sl * nd);
-    if (rc != ZERO_OK) return rc;
+    if (sl == 0) continue;
+    const int k = T.n;
+    const int64_t so = L->bucket_shard_off(b), fo = L->bucket_padded_off(b);
+    const int64_t tiles = (sl + kGatherTile - 1) / kGatherTile;
+    T.shard_off[k] = so;
+    T.flat_off[k] = fo;
+    T.slice[k] = sl;
+    T.tiles[k] = (uint32_t)tiles;
+    T.item0[k + 1] = T.item0[k] + (uint32_t)(tiles * nd);  // < 2^32: checked above
+    if (base_vec && so % 8 == 0 && fo % 8 == 0 && sl % 8 == 0) T.vec |= 1ull << k;
+    T.n = k + 1;
+    if (T.n == kGatherTab) {
+      const int rc = flush();
+      if (rc != ZERO_OK) return rc;
+    }
   }
-  return ZERO_OK;
+  return T.n > 0 ? flush() : ZERO_OK;
 }
 
 int zero_reshard(const zero_layout* src, const void* const* src_shards, const zero_layout* dst,

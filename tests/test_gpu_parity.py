@@ -863,6 +863,27 @@ def test_gather_params_gpt2s_full():
     assert_bitwise(u16(out), oracle.gather(sh_h, pl), "gpt2s gather")
 
 
+def test_gather_params_gpt2s_fsdp2_full_and_tensor_range():
+    """Per-parameter layout (148 tensors, table launches of 48): the whole
+    gather, and a tensor range that leaves every other slot untouched."""
+    w = workloads.get("gpt2s_fsdp2")
+    pl = oracle.plan(w.numel, 0, w.n_d, rows=w.rows)
+    sh_h = _rank_shards_bf16(pl, w.n_d, 4)
+    sh = [torch.from_numpy(x.view(np.int16)).to(DEV) for x in sh_h]
+    L = z.Layout(w.numel, 0, w.n_d, 0, rows=w.rows)
+    exp = oracle.gather(sh_h, pl)
+    out = torch.full((pl.padded_total,), CANARY, dtype=torch.int16, device=DEV)
+    z.zero_gather_params(L, sh, out)
+    out2 = torch.full((pl.padded_total,), CANARY, dtype=torch.int16, device=DEV)
+    z.zero_gather_params(L, sh, out2, 50, 120)
+    torch.cuda.synchronize()
+    assert_bitwise(u16(out), exp, "gpt2s_fsdp2 gather")
+    lo, hi = int(pl.padded_off[50]), int(pl.padded_off[119] + pl.padded_len[119])
+    got = u16(out2)
+    assert_bitwise(got[lo:hi], exp[lo:hi], "tensor range 50..119")
+    assert (got[:lo].view(np.int16) == CANARY).all() and (got[hi:].view(np.int16) == CANARY).all()
+
+
 RESHARD = [
     # numel, (cap, n_d) source, (cap, n_d, rank) destination
     ([1000, 37, 4096, 3], (1500, 4), (0, 2, 1)),
@@ -1068,7 +1089,9 @@ def test_llama8b_fsdp2_sampled():
 
 @pytest.mark.parametrize("shapes,n_d", [([(5, 3), (7,), (1, 9), (16, 16)], 4),
                                         ([(129, 64), (1000,), (2, 3)], 64),
-                                        ([(4, 2), (4, 2), (4, 2)], 2)])
+                                        ([(4, 2), (4, 2), (4, 2)], 2),
+                                        ([((k * 7) % 41 + 1, (k * 5) % 13 + 1) if k % 9
+                                          else (64, 64) for k in range(75)], 4)])
 def test_dim0_gather_and_reshard(shapes, n_d):
     numel = [int(np.prod(s)) for s in shapes]
     rows = [s[0] for s in shapes]
