@@ -949,7 +949,8 @@ def test_reshard_gpt2s_state_8_to_4_ranks_round_trip():
 @pytest.mark.timeout(600)
 def test_llama8b_pack_gather_reshard_full_size():
     """Full-size pack, gather and re-cut on the Llama-3-8B list (8.03e9
-    elements; each call is split over several launches).  Values are keyed
+    elements; each call is split over several launches), bucketed and
+    per-parameter (dim-0) shards.  Values are keyed
     by stream position, so the expected value of every position is known:
     sampled positions are checked against the generator and the oracle's
     layout, and every position against the concatenated tensors."""
@@ -1006,6 +1007,32 @@ def test_llama8b_pack_gather_reshard_full_size():
     assert_bitwise(dst[torch.from_numpy(xs1).to(DEV)].cpu().numpy().view(np.uint16),
                    synth.values_at(xs1, key, *dist, synth.OUT_BF16), "re-cut shard")
     assert torch.equal(dst, stream_all), "re-cut shard differs from the tensors in stream order"
+    del shards
+    torch.cuda.empty_cache()
+
+    say("  per-parameter (dim-0) shards: gather, and re-cut for one bucketed rank")
+    rows = [sh[1][0] for sh in w.shapes]
+    pd = oracle.plan(w.numel, 0, 8, rows=rows)
+    Ld = z.Layout(w.numel, 0, 8, 0, rows=rows)
+    dshards = []
+    for q in range(8):
+        sh = torch.empty(pd.shard_len, dtype=torch.int16, device=DEV)
+        synth.fill_device(sh, synth.shard_segments(pd.stream_off, pd.len, pd.padded_len,
+                                                   pd.shard_off, 8, q), key, *dist)
+        dshards.append(sh)
+    dst.fill_(CANARY)
+    z.zero_reshard(Ld, dshards, L1, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, stream_all), "dim-0 re-cut differs from the tensors in stream order"
+    dfull = torch.full((pd.padded_total,), CANARY, dtype=torch.int16, device=DEV)
+    z.zero_gather_params(Ld, dshards, dfull)
+    torch.cuda.synchronize()
+    dpos = np.unique(rng.integers(0, pd.padded_total, 1 << 18))
+    db = np.searchsorted(pd.padded_off, dpos, side="right") - 1
+    doff = dpos - pd.padded_off[db]
+    dxs = np.where(doff < pd.len[db], pd.stream_off[db] + doff, -1)
+    assert_bitwise(dfull[torch.from_numpy(dpos).to(DEV)].cpu().numpy().view(np.uint16),
+                   synth.values_at(dxs, key, *dist, synth.OUT_BF16), "dim-0 gathered buffer")
 
 
 # ------------------------------------------------------------------ FSDP2 per-parameter layout
