@@ -380,7 +380,19 @@ def next_rows(z, synth, w, L, holder, timed, placement):
     ms = timed(lambda: z.zero_gather_params(L, inp.grads, inp.pout))
     row("gather", "gather_kernel", "llama8b: 8 rank shards -> 8,030,261,248-element flat "
         "buffer", 4 * P, ms)
-    del inp, shard_out
+    # the same two movements for the per-parameter (dim-0) layout: its
+    # gather (one table launch per 48 tensors) and a re-cut of its bf16
+    # shards for 4 bucketed ranks
+    if Ld.padded <= inp.pout.numel():
+        ms = timed(lambda: z.zero_gather_params(Ld, inp.grads, inp.pout[:Ld.padded]))
+        row("gather_fsdp2", "gather_table_kernel", "llama8b_fsdp2: 8 rank shards -> "
+            f"{Ld.padded:,}-element flat buffer", 4 * Ld.padded, ms)
+    L4b = z.Layout(w.numel, w.cap, 4, 3)
+    dst16 = torch.empty(L4b.shard, dtype=torch.int16, device=dev)
+    ms = timed(lambda: z.zero_reshard(Ld, inp.grads, L4b, dst16), reps=5)
+    row("reshard_fsdp2", "reshard_table_kernel<u16>", "llama8b bf16 params: 8 dim-0 shards -> "
+        f"rank 3 of 4 bucketed ({L4b.shard} elements)", 4 * L4b.shard, ms)
+    del inp, shard_out, dst16
     torch.cuda.empty_cache()
     # fp32 contributions
     inp, _ = make_inputs(z, synth, w, L, placement, grad_dtype=torch.float32)
