@@ -175,6 +175,49 @@ def test_llama70b_sampled(name):
 
 
 # ------------------------------------------------------------------ edge cases
+@pytest.mark.timeout(600)
+def test_shard_beyond_2_pow_31_elements_sampled():
+    """A shard of 2^31 + 4099 elements (64-bit indexing everywhere; ragged
+    tail), N_d = 2, rank 1, All-Gather slot output 2^32 + 8198 elements
+    away from the start: sampled against the oracle."""
+    S = (1 << 31) + 4099
+    w = workloads.Workload("flat1m", [2 * S], 0, 2, 1, "compact", "ag_slot", 7, 1,
+                           ("normal", 1e-3), ("normal", 0.02), ("normal", 1e-4),
+                           ("absnormal", 1e-6))
+    case = Case(w)
+    assert case.S == S
+    idx = np.concatenate([sample_indices(S, case.pl, n_random=1 << 16),
+                          np.arange((1 << 31) - 64, (1 << 31) + 64)])
+    case.__init__(w, sample_idx=idx)
+    stats = run_steps(case)
+    assert stats["param"] == case.idx.size
+
+
+@pytest.mark.timeout(300)
+def test_accumulate_beyond_2_pow_31_elements_sampled():
+    """no_sync accumulation over 2^31 + 5 elements (overwrite, add, then add
+    with bf16 emit and no fp32 store), sampled against the oracle."""
+    n = (1 << 31) + 5
+    segs = [(0, 0, n, 0)]
+    acc = torch.empty(n, dtype=torch.float32, device=DEV)
+    g = torch.empty(n, dtype=torch.int16, device=DEV)
+    emit = torch.empty(n, dtype=torch.int16, device=DEV)
+    rng = np.random.default_rng(3)
+    xs = np.unique(np.concatenate([rng.integers(0, n, 1 << 16), np.arange(n - 64, n),
+                                   np.arange((1 << 31) - 64, (1 << 31) + 5)]))
+    o_acc = np.zeros(xs.size, np.float32)
+    for k, flags in enumerate((z.ACC_OVERWRITE, 0, z.ACC_EMIT_BF16 | z.ACC_NO_STORE)):
+        key = synth.key("accum1p3b", "micro_grad", 0, k, 1)
+        synth.fill_device(g, segs, key, "normal", 2e-3)
+        z.zero_grad_accumulate(acc, g, 0.25, flags, emit if flags & z.ACC_EMIT_BF16 else None)
+        o_out = oracle.accumulate(o_acc, synth.values_at(xs, key, "normal", 2e-3, synth.OUT_BF16),
+                                  0.25, overwrite=(k == 0), store_acc=(k < 2), emit=(k == 2))
+    torch.cuda.synchronize()
+    sel = torch.from_numpy(xs).to(DEV)
+    assert_bitwise(acc[sel].cpu().numpy(), o_acc, "accumulator")
+    assert_bitwise(emit[sel].cpu().numpy().view(np.uint16), o_out, "emitted bf16")
+
+
 EDGE = [
     # numel, cap, n_d, rank, grad_layout, out_mode
     ([1000, 37, 4096, 3], 1500, 4, 3, "flat", "ag_slot"),
