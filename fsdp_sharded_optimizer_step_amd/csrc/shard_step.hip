@@ -24,6 +24,7 @@
 // the launch shape.  Each rank count that matters gets its own unrolled
 // instantiation; for large N_d the rank loads are issued in groups so that
 // registers stay within budget while enough bytes are in flight.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <vector>
@@ -422,15 +423,20 @@ void fill_args(Args& A, const Call& c, const Region& reg) {
   A.slot_out = c.slot_out;
 }
 
+// Compute units of the current device, cached per device (relaxed atomics:
+// concurrent callers may both query, and store the same value).
 int cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cached[dev]) return cached[dev];
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     n = 256;
-  if (dev < 64) cached[dev] = n;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
