@@ -117,6 +117,9 @@ def make_inputs(z, synth, w, L, placement="tuned", grad_dtype=None, accumulators
     om = z.OUT_AG_SLOT if w.out_mode == "ag_slot" else z.OUT_SHARD
     specs = zp.step_specs(L, grad_dtype=grad_dtype, grad_layout=gl, out_mode=om,
                           accumulators=accumulators)
+    if placement not in ("tuned", "planned", "separate"):
+        raise ValueError(placement)
+    pool = None
     if placement in ("tuned", "planned"):
         choose = None
         if placement == "tuned":
@@ -124,14 +127,19 @@ def make_inputs(z, synth, w, L, placement="tuned", grad_dtype=None, accumulators
                 call = step_call(z, L, z.AdamW(**w.hp), w.t_first, gl, om, fused=accumulators)
             timed = make_timer(torch.cuda.current_stream())
             choose = lambda v: timed(lambda: call(v), reps=4)
-        pool = zp.Pool(specs, device=dev, slack=TUNE_SLACK if placement == "tuned" else 0,
-                       choose=choose)
-        views = pool.views
-    elif placement == "separate":
-        pool = None
+        try:
+            pool = zp.Pool(specs, device=dev, slack=TUNE_SLACK if placement == "tuned" else 0,
+                           choose=choose)
+            views = pool.views
+        except torch.cuda.OutOfMemoryError:
+            # a device without room for the pool's spare lanes: one
+            # allocation per buffer instead (reported as such)
+            torch.cuda.empty_cache()
+            print(f"# {placement} pool does not fit; separate allocations", file=sys.stderr,
+                  flush=True)
+            placement = "separate"
+    if placement == "separate":
         views = {name: torch.empty(n, dtype=dt, device=dev) for name, n, dt, _ in specs}
-    else:
-        raise ValueError(placement)
     so, ln, po, pln, sh = (list(x) for x in zip(*L.buckets()))
     segs = synth.shard_segments(so, ln, pln, sh, w.n_d, w.rank)
     gsegs = [(p0, s0, l, pl - l) for s0, l, p0, pl in zip(so, ln, po, pln)] if flat else segs
@@ -528,6 +536,7 @@ def main():
     print(f"# workload {w.name}: S={S} P={P} N_d={w.n_d} buckets={L.n_buckets}", file=sys.stderr,
           flush=True)
     inp, segs = make_inputs(z, synth, w, L, args.placement)
+    placement_used = "separate" if inp.pool is None else args.placement
     hp = z.AdamW(**w.hp)
     gl = z.GRAD_COMPACT if w.grad_layout == "compact" else z.GRAD_FLAT
     om = z.OUT_AG_SLOT if w.out_mode == "ag_slot" else z.OUT_SHARD
@@ -588,7 +597,7 @@ def main():
     # the same step on one torch allocation per buffer, for comparison
     other = None
     if not args.no_aux:
-        alt = "separate" if args.placement != "separate" else "tuned"
+        alt = "separate" if placement_used != "separate" else "tuned"
         inp, _ = make_inputs(z, synth, w, L, alt)
         ms_alt = make_timer(stream)(lambda: z.zero_shard_step(L, hp, t, inp.grads, gl, *inp.state,
                                                               inp.pout, om), reps=10)
@@ -625,7 +634,7 @@ def main():
                    "padded_elems": P, "n_d": w.n_d, "rank": w.rank, "buckets": L.n_buckets,
                    "grad_layout": w.grad_layout, "out_mode": w.out_mode,
                    "bytes_per_elem": bytes_per_elem, "io": "bf16 grads and params, f32 state",
-                   "placement": args.placement, "placement_tuning": tuning},
+                   "placement": placement_used, "placement_tuning": tuning},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "kernel": step_kernel_name(w.n_d, w.grad_layout == "flat"
