@@ -104,6 +104,7 @@ def pin_calls(with_exhaustive: bool):
     calls += [(P.test_adamw_ten_steps_vs_torch_normwise, {})]
     calls += [(P.test_layout_brute_force, {"seed": s}) for s in range(40)]
     calls += [(P.test_fsdp2_layout_brute_force, {"seed": s}) for s in range(25)]
+    calls += [(P.test_fsdp2_slices_agree_with_torch_chunk, {"seed": s}) for s in range(20)]
     calls += [(P.test_gather_locate_reshard_brute_force, {"seed": s}) for s in range(25)]
     calls += [(P.test_layout_workload_sizes_closed_form, {"name": n}) for n in workloads.NAMES]
     calls += [(P.test_layout_padded_tail_workload, {})]

@@ -284,6 +284,36 @@ def test_fsdp2_layout_brute_force(seed):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("seed", range(20))
+def test_fsdp2_slices_agree_with_torch_chunk(seed):
+    """The per-parameter reading (rank r owns rows [r*c, (r+1)*c) with
+    c = ceil(rows/N_d), missing rows are padding) is PyTorch's chunk-then-pad
+    convention: the real part of rank r's slice of every tensor is
+    torch.chunk(t, N_d, dim=0)[r] (or nothing when chunk returns fewer
+    pieces), the rest of the slice is zero padding."""
+    import torch
+    rng = np.random.default_rng(900 + seed)
+    shapes = [tuple(int(v) for v in rng.integers(1, 11, int(rng.integers(1, 3))))
+              for _ in range(int(rng.integers(1, 6)))]
+    n_d = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 16]))
+    numel = [int(np.prod(x)) for x in shapes]
+    pl = oracle.plan(numel, 0, n_d, rows=[x[0] for x in shapes])
+    offs = np.concatenate([[0], np.cumsum(numel)])
+    values = [np.arange(1 + offs[t], 1 + offs[t] + n, dtype=np.uint16)
+              for t, n in enumerate(numel)]
+    packed = oracle.pack(values, pl)
+    for r in range(n_d):
+        shard = oracle.slice_shard(packed, pl, r)
+        for t, shp in enumerate(shapes):
+            sl = int(pl.padded_len[t]) // n_d
+            got = shard[int(pl.shard_off[t]):int(pl.shard_off[t]) + sl]
+            chunks = torch.chunk(torch.from_numpy(values[t].astype(np.int64)).reshape(shp), n_d,
+                                 dim=0)
+            real = chunks[r].reshape(-1).numpy() if r < len(chunks) else np.zeros(0, np.int64)
+            assert np.array_equal(got[:real.size].astype(np.int64), real)
+            assert not got[real.size:].any()
+
+
 @pytest.mark.parametrize("name", workloads.NAMES)
 def test_layout_workload_sizes_closed_form(name):
     """Fixed-cut buckets: nb = ceil(psi/C), S = (nb-1)*ceil(C/n_d) + ceil(last/n_d)."""
