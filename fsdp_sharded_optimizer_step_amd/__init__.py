@@ -8,10 +8,11 @@ from .binding import (ACC_EMIT_BF16, ACC_NO_STORE, ACC_OVERWRITE, DTYPE_BF16, DT
                       GRAD_COMPACT, GRAD_FLAT, OUT_AG_SLOT, OUT_SHARD, AdamW, Layout, ZeroError,
                       load, zero_bucket_pack, zero_gather_params, zero_grad_accumulate,
                       zero_reshard, zero_shard_step, zero_shard_step_accumulate,
-                      zero_step_scalars)
+                      zero_shard_step_buckets, zero_step_scalars)
 
 __all__ = ["ACC_EMIT_BF16", "ACC_NO_STORE", "ACC_OVERWRITE", "DTYPE_BF16", "DTYPE_F32",
            "GRAD_COMPACT", "GRAD_FLAT",
            "OUT_AG_SLOT", "OUT_SHARD", "AdamW", "Layout", "ZeroError", "load",
            "zero_bucket_pack", "zero_gather_params", "zero_grad_accumulate", "zero_reshard",
-           "zero_shard_step", "zero_shard_step_accumulate", "zero_step_scalars"]
+           "zero_shard_step", "zero_shard_step_accumulate", "zero_shard_step_buckets",
+           "zero_step_scalars"]

@@ -27,7 +27,7 @@ EXPORTS = ("zero_layout_create", "zero_layout_destroy", "zero_layout_psi", "zero
            "zero_layout_bucket", "zero_layout_tensor", "zero_bucket_pack", "zero_grad_accumulate",
            "zero_shard_step", "zero_shard_step_ex", "zero_step_scalars", "zero_strerror",
            "zero_gather_params", "zero_reshard", "zero_layout_create_dim0", "zero_layout_kind",
-           "zero_shard_step_accumulate", "zero_placement_plan")
+           "zero_shard_step_accumulate", "zero_placement_plan", "zero_shard_step_buckets")
 
 
 class ZeroError(RuntimeError):
@@ -87,6 +87,9 @@ def load():
     lib.zero_shard_step_ex.argtypes = [vp, C.POINTER(_AdamW), C.c_int64, C.POINTER(vp),
                                        C.c_int32, vp, vp, vp, vp, C.c_int32, vp,
                                        C.POINTER(_Options), vp]
+    lib.zero_shard_step_buckets.argtypes = [vp, C.POINTER(_AdamW), C.c_int64, C.c_int64,
+                                            C.c_int64, C.POINTER(vp), C.c_int32, vp, vp, vp,
+                                            vp, C.c_int32, vp, C.POINTER(_Options), vp]
     lib.zero_shard_step_accumulate.argtypes = [vp, C.POINTER(_AdamW), C.c_int64, C.POINTER(vp),
                                                C.POINTER(vp), C.c_float, C.c_int32, C.c_int32,
                                                vp, vp, vp, vp, C.c_int32, vp,
@@ -250,6 +253,26 @@ def zero_shard_step(layout: Layout, hp: AdamW, t: int, rank_grads, grad_layout: 
         opt = _Options(DTYPE_F32 if f32 else DTYPE_BF16, blocks, threads, path)
         _check("zero_shard_step_ex", load().zero_shard_step_ex(*args, C.byref(opt),
                                                                 _stream_ptr(stream)))
+
+
+def zero_shard_step_buckets(layout: Layout, hp: AdamW, t: int, bucket_begin: int,
+                            bucket_end: int, rank_grads, grad_layout: int, master, exp_avg,
+                            exp_avg_sq, param_out, out_mode: int, reduced_grad_out=None,
+                            stream=None, launch=None):
+    """The shard step of buckets [bucket_begin, bucket_end) only; the
+    buffers are the whole-shard ones of zero_shard_step."""
+    import torch
+    if len(rank_grads) != layout.n_d:
+        raise ValueError("zero_shard_step_buckets: one contribution per rank is required")
+    f32 = len(rank_grads) > 0 and rank_grads[0] is not None and rank_grads[0].dtype == torch.float32
+    blocks, threads, path = launch if launch is not None else (0, 0, 0)
+    opt = _Options(DTYPE_F32 if f32 else DTYPE_BF16, blocks, threads, path)
+    _check("zero_shard_step_buckets", load().zero_shard_step_buckets(
+        layout.handle, C.byref(hp._c()), int(t), int(bucket_begin), int(bucket_end),
+        _ptr_array(rank_grads, "rank_grads", _dev32 if f32 else _dev16), grad_layout,
+        _dev32(master, "master"), _dev32(exp_avg, "exp_avg"), _dev32(exp_avg_sq, "exp_avg_sq"),
+        _dev16(param_out, "param_out"), out_mode, _dev32(reduced_grad_out, "reduced_grad_out"),
+        C.byref(opt), _stream_ptr(stream)))
 
 
 def zero_shard_step_accumulate(layout: Layout, hp: AdamW, t: int, rank_acc, rank_micro,

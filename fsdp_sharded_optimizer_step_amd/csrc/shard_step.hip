@@ -606,14 +606,17 @@ int parse_options(const zero_step_options* opt, LaunchShape& ls) {
 // Validates everything common to the step entry points, plans the launches
 // and enqueues them.  `ins`/`in_bytes`: the contribution buffers of every
 // rank (two per rank when fused), each of in_bytes bytes.
+// Buckets [b0, b1) of the layout are updated (all of them for the
+// whole-shard entry points); buffers are always the full-size ones.
 int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int32_t grad_layout,
              int32_t out_mode, const LaunchShape& ls, const void* const* ins, int n_ins,
-             const int64_t* in_bytes, hipStream_t stream) {
+             const int64_t* in_bytes, int64_t b0, int64_t b1, hipStream_t stream) {
   if (grad_layout != ZERO_GRAD_COMPACT && grad_layout != ZERO_GRAD_FLAT) return ZERO_EINVAL;
   if (out_mode != ZERO_OUT_AG_SLOT && out_mode != ZERO_OUT_SHARD) return ZERO_EINVAL;
+  if (b0 < 0 || b1 > L->nb || b0 > b1) return ZERO_ERANGE;
   const int32_t nd = L->n_d;
   const int64_t S = L->S, P = L->P;
-  if (S == 0) return ZERO_OK;
+  if (S == 0 || b0 == b1) return ZERO_OK;
   if (!c.master || !c.m || !c.v || !c.pout) return ZERO_EINVAL;
   for (int q = 0; q < n_ins; ++q)
     if (!ins[q]) return ZERO_EINVAL;
@@ -663,7 +666,7 @@ int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int3
       T.vec = 0;
       return rc;
     };
-    for (int64_t b = 0; b < L->nb; ++b) {
+    for (int64_t b = b0; b < b1; ++b) {
       const int64_t sl = L->bucket_slice(b);
       if (sl == 0) continue;
       const int64_t i0 = L->bucket_shard_off(b), f0 = L->bucket_padded_off(b) + r * sl;
@@ -683,36 +686,51 @@ int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int3
     return flush();
   }
 
-  // Bucketed layout.  Without flat addressing the shard is one plain range.
-  // With it: part 0 = the full buckets, part 1 = the last bucket; one vector
-  // launch covers both when every vector address is aligned, otherwise the
-  // parts that are not aligned go to the scalar kernel.
+  // Without flat addressing the buckets' slices are one plain shard range.
+  // With it (bucketed layout): part 0 = the full buckets of the range, part
+  // 1 = the last bucket if it is in the range; one vector launch covers both
+  // when every vector address is aligned, otherwise the parts that are not
+  // aligned go to the scalar kernel.
   std::vector<Region> regs;
   std::vector<bool> vec;
+  const int64_t i_begin = L->bucket_shard_off(b0);
+  const int64_t i_end = b1 < L->nb ? L->bucket_shard_off(b1) : S;
+  const int64_t n_all = i_end - i_begin;
   if (!map) {
-    regs.push_back(Region{0, S, S, S, 0, 0, 0});
-    vec.push_back(allow_vec);
+    regs.push_back(Region{i_begin, n_all, n_all, n_all, 0, 0, 0});
+    vec.push_back(allow_vec && i_begin % 8 == 0);
   } else if (L->nb == 1 || L->s_last == L->s_full) {
-    const bool one = L->nb == 1;
-    regs.push_back(Region{0, S, S, L->s_full, L->p_full, r * L->s_full, 0});
-    vec.push_back(allow_vec && (r * L->s_full) % 8 == 0 &&
+    // every bucket has the same slice: one affine part
+    const bool one = b1 - b0 == 1;
+    const int64_t flat0 = b0 * L->p_full + r * L->s_full;
+    regs.push_back(Region{i_begin, n_all, n_all, L->s_full, L->p_full, flat0, 0});
+    vec.push_back(allow_vec && i_begin % 8 == 0 && flat0 % 8 == 0 &&
                   (one || (L->s_full % 8 == 0 && L->p_full % 8 == 0)));
   } else {
-    const int64_t n0 = (L->nb - 1) * L->s_full;
+    const bool has_last = b1 == L->nb;
+    const int64_t nf = (has_last ? L->nb - 1 : b1) - b0;  // full buckets in the range
+    const int64_t n0 = nf * L->s_full;
+    const int64_t flat0 = b0 * L->p_full + r * L->s_full;
     const int64_t flat1 = (L->nb - 1) * L->p_full + r * L->s_last;
-    const bool v0 = allow_vec && L->s_full % 8 == 0 && L->p_full % 8 == 0;
-    const bool v1 = allow_vec && flat1 % 8 == 0;
-    if (v0 && v1) {
-      regs.push_back(Region{0, n0, S, L->s_full, L->p_full, r * L->s_full, flat1});
-      vec.push_back(true);
-    } else if (v0) {
-      regs.push_back(Region{0, n0, n0, L->s_full, L->p_full, r * L->s_full, 0});
-      vec.push_back(true);
-      regs.push_back(Region{n0, L->s_last, L->s_last, L->s_last, L->p_last, flat1, 0});
-      vec.push_back(false);
+    if (nf == 0) {
+      // the last bucket alone
+      regs.push_back(Region{i_begin, L->s_last, L->s_last, L->s_last, L->p_last, flat1, 0});
+      vec.push_back(allow_vec && i_begin % 8 == 0 && flat1 % 8 == 0);
     } else {
-      regs.push_back(Region{0, n0, S, L->s_full, L->p_full, r * L->s_full, flat1});
-      vec.push_back(false);
+      const bool v0 = allow_vec && L->s_full % 8 == 0 && L->p_full % 8 == 0;
+      const bool v1 = !has_last || (allow_vec && flat1 % 8 == 0);
+      if (v0 && v1) {
+        regs.push_back(Region{i_begin, n0, n_all, L->s_full, L->p_full, flat0, flat1});
+        vec.push_back(true);
+      } else if (v0) {
+        regs.push_back(Region{i_begin, n0, n0, L->s_full, L->p_full, flat0, 0});
+        vec.push_back(true);
+        regs.push_back(Region{i_begin + n0, L->s_last, L->s_last, L->s_last, L->p_last, flat1, 0});
+        vec.push_back(false);
+      } else {
+        regs.push_back(Region{i_begin, n0, n_all, L->s_full, L->p_full, flat0, flat1});
+        vec.push_back(false);
+      }
     }
   }
 
@@ -748,6 +766,37 @@ int zero_step_scalars(const zero_adamw* hp, int64_t t, float out[8]) {
   return ZERO_OK;
 }
 
+int zero_shard_step_buckets(const zero_layout* L, const zero_adamw* hp, int64_t t,
+                            int64_t bucket_begin, int64_t bucket_end,
+                            const void* const* rank_grads, int32_t grad_layout, float* master,
+                            float* exp_avg, float* exp_avg_sq, uint16_t* param_out,
+                            int32_t out_mode, float* reduced_grad_out,
+                            const zero_step_options* opt, hipStream_t stream) {
+  if (!L || !hp || !rank_grads || t < 1 || !hp_ok(*hp)) return ZERO_EINVAL;
+  int gt = GT_BF16;
+  if (opt) {
+    if (opt->grad_dtype != ZERO_DTYPE_BF16 && opt->grad_dtype != ZERO_DTYPE_F32)
+      return ZERO_EINVAL;
+    gt = opt->grad_dtype == ZERO_DTYPE_F32 ? GT_F32 : GT_BF16;
+  }
+  LaunchShape ls;
+  if (parse_options(opt, ls) != ZERO_OK) return ZERO_EINVAL;
+  const int64_t n_in = grad_layout == ZERO_GRAD_FLAT ? L->P : L->S;
+  std::vector<int64_t> bytes((size_t)L->n_d, contrib_bytes(gt) * n_in);
+  Call c{};
+  c.g = rank_grads;
+  c.a = nullptr;
+  c.gt = gt;
+  c.acc_scale = 0.0f;
+  c.master = master;
+  c.m = exp_avg;
+  c.v = exp_avg_sq;
+  c.gout = reduced_grad_out;
+  c.pout = param_out;
+  return run_step(L, hp, t, c, grad_layout, out_mode, ls, rank_grads, L->n_d, bytes.data(),
+                  bucket_begin, bucket_end, stream);
+}
+
 int zero_shard_step_ex(const zero_layout* L, const zero_adamw* hp, int64_t t,
                        const void* const* rank_grads, int32_t grad_layout, float* master,
                        float* exp_avg, float* exp_avg_sq, uint16_t* param_out, int32_t out_mode,
@@ -774,8 +823,8 @@ int zero_shard_step_ex(const zero_layout* L, const zero_adamw* hp, int64_t t,
   c.v = exp_avg_sq;
   c.gout = reduced_grad_out;
   c.pout = param_out;
-  return run_step(L, hp, t, c, grad_layout, out_mode, ls, rank_grads, L->n_d, bytes.data(),
-                  stream);
+  return run_step(L, hp, t, c, grad_layout, out_mode, ls, rank_grads, L->n_d, bytes.data(), 0,
+                  L->nb, stream);
 }
 
 int zero_shard_step_accumulate(const zero_layout* L, const zero_adamw* hp, int64_t t,
@@ -810,8 +859,8 @@ int zero_shard_step_accumulate(const zero_layout* L, const zero_adamw* hp, int64
   c.v = exp_avg_sq;
   c.gout = reduced_grad_out;
   c.pout = param_out;
-  return run_step(L, hp, t, c, grad_layout, out_mode, ls, ins.data(), 2 * nd, bytes.data(),
-                  stream);
+  return run_step(L, hp, t, c, grad_layout, out_mode, ls, ins.data(), 2 * nd, bytes.data(), 0,
+                  L->nb, stream);
 }
 
 int zero_shard_step(const zero_layout* L, const zero_adamw* hp, int64_t t,

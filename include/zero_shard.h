@@ -294,6 +294,28 @@ int zero_shard_step_accumulate(const zero_layout* layout, const zero_adamw* hp, 
                                float* reduced_grad_out_dev, const zero_step_options* opt,
                                hipStream_t stream);
 
+/* zero_shard_step_ex restricted to buckets [bucket_begin, bucket_end) of the
+ * layout ("Zero Redundancy Optimizer (ZeRO)", ZeRO-2: gradients are reduced
+ * bucket by bucket as they become ready).  The update of an element reads
+ * only that element's contributions and state, so a caller may step each
+ * bucket's slice as soon as its reduction has landed; stepping every bucket
+ * once, in any grouping and order, gives the same bits as one
+ * zero_shard_step_ex call.
+ *
+ * All buffers are the full-size ones of zero_shard_step_ex (contributions of
+ * S or P values, S-element state, S- or P-element output); only the slices
+ * of the named buckets are read and written.  For a dim-0 layout a bucket is
+ * a tensor.  bucket_begin == bucket_end is a no-op.
+ * Errors: as for zero_shard_step_ex, plus ZERO_ERANGE when
+ * 0 <= bucket_begin <= bucket_end <= n_buckets does not hold. */
+int zero_shard_step_buckets(const zero_layout* layout, const zero_adamw* hp, int64_t t,
+                            int64_t bucket_begin, int64_t bucket_end,
+                            const void* const* rank_grads_dev, int32_t grad_layout,
+                            float* master_dev, float* exp_avg_dev, float* exp_avg_sq_dev,
+                            uint16_t* param_out_dev, int32_t out_mode,
+                            float* reduced_grad_out_dev, const zero_step_options* opt,
+                            hipStream_t stream);
+
 /* --------------------------------------------------------- parameter gather
  * ("Zero Redundancy Optimizer (ZeRO)": ZeRO-1/2 All-Gather the updated
  * parameters after the step; ZeRO-3 All-Gathers each layer's parameters

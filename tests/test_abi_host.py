@@ -237,6 +237,35 @@ def test_fused_accumulate_step_argument_errors():
     assert call(layout=z.Layout([], 0, 2, 0).handle) == E.ZERO_OK
 
 
+def test_bucket_range_step_argument_errors():
+    """zero_shard_step_buckets checks its bucket range and then validates
+    like zero_shard_step_ex; an empty range succeeds without a launch."""
+    lib = z.load()
+    E = z.binding
+    L = z.Layout([40, 24, 100], 32, 2, 1)            # 5 buckets of 32 and one of 4
+    hp = binding._AdamW(1e-3, 0.9, 0.95, 1e-8, 0.1)
+    g = (C.c_void_p * 2)(0x100000, 0x200000)
+
+    def call(b0=0, b1=None, grads=g, master=0x300000, m=0x400000, p=0x600000, om=1, opt=None):
+        b1 = L.n_buckets if b1 is None else b1
+        return lib.zero_shard_step_buckets(L.handle, C.byref(hp), 1, b0, b1, grads, 0, master,
+                                           m, 0x500000, p, om, None, opt, None)
+
+    nb = L.n_buckets
+    assert call(b0=-1) == E.ZERO_ERANGE
+    assert call(b1=nb + 1) == E.ZERO_ERANGE
+    assert call(b0=2, b1=1) == E.ZERO_ERANGE
+    assert call(b0=1, b1=1) == E.ZERO_OK
+    assert call(b0=nb, b1=nb) == E.ZERO_OK
+    assert call(b0=0, b1=2, master=None) == E.ZERO_EINVAL
+    assert call(b0=0, b1=2, grads=(C.c_void_p * 2)(0x100000, None)) == E.ZERO_EINVAL
+    assert call(b0=0, b1=2, m=0x300000 + 16) == E.ZERO_EOVERLAP
+    assert call(b0=1, b1=2, opt=C.byref(binding._Options(0, 0, 96, 0))) == E.ZERO_EINVAL
+    assert call(b0=1, b1=2, opt=C.byref(binding._Options(5, 0, 0, 0))) == E.ZERO_EINVAL
+    assert lib.zero_shard_step_buckets(None, C.byref(hp), 1, 0, 1, g, 0, 0x300000, 0x400000,
+                                       0x500000, 0x600000, 1, None, None, None) == E.ZERO_EINVAL
+
+
 def test_accumulate_and_pack_argument_errors():
     lib = z.load()
     E = z.binding

@@ -598,6 +598,130 @@ def test_gpu_bf16_cast_exhaustive():
             say(f"  cast chunk {c} ok")
 
 
+# ------------------------------------------------------------------ bucket ranges
+BUCKET_RANGES = [
+    # numel, cap, n_d, rank, grad_layout, out_mode
+    ([70000, 3], 16384, 8, 7, "flat", "ag_slot"),           # ragged last bucket, unaligned
+    ([1000, 37, 4096, 3], 1500, 4, 3, "flat", "ag_slot"),   # slices of 375: scalar path
+    ([4096 * 7 + 5], 4096, 7, 6, "flat", "shard"),
+    ([50000], 8008, 8, 3, "compact", "ag_slot"),
+    ([20000, 20001], 4000, 16, 15, "compact", "shard"),
+    ([64 * 300 + 1], 6400, 64, 63, "flat", "ag_slot"),
+    ([8192 * 6], 8192, 8, 2, "flat", "ag_slot"),            # six equal buckets
+    ([100 * 97], 1000, 100, 99, "compact", "shard"),         # runtime rank count
+]
+
+
+def _step_buckets(case, t, grads, b0, b1):
+    w = case.w
+    gl = z.GRAD_FLAT if w.grad_layout == "flat" else z.GRAD_COMPACT
+    om = z.OUT_AG_SLOT if w.out_mode == "ag_slot" else z.OUT_SHARD
+    z.zero_shard_step_buckets(case.L, case.hp_z, t, b0, b1, grads, gl, case.master, case.m,
+                              case.v, case.pout, om, case.gout)
+
+
+def _random_ranges(nb, rng):
+    cuts = sorted(set(int(c) for c in rng.integers(0, nb + 1, 4)) | {0, nb})
+    ranges = list(zip(cuts[:-1], cuts[1:]))
+    rng.shuffle(ranges)
+    return ranges
+
+
+@pytest.mark.parametrize("numel,cap,n_d,rank,gl,om", BUCKET_RANGES)
+def test_bucket_ranges_in_any_order_equal_the_oracle(numel, cap, n_d, rank, gl, om):
+    """Every bucket stepped once per step, in random groups and order, gives
+    the oracle's whole-shard step bit for bit."""
+    case = _edge_case(numel, cap, n_d, rank, gl, om)
+    rng = np.random.default_rng(sum(numel) + 31 * n_d)
+    case.init_state_gpu()
+    case.init_state_oracle()
+    for t in (1, 2, 3):
+        ranges = _random_ranges(case.L.n_buckets, rng)
+        say(f"  buckets numel={numel} cap={cap} n_d={n_d} r={rank} {gl} {om} t={t}: {ranges}")
+        grads = case.grads_gpu(t)
+        for b0, b1 in ranges:
+            _step_buckets(case, t, grads, b0, b1)
+        case.step_oracle(t, case.grads_oracle(t))
+    torch.cuda.synchronize()
+    case.compare("bucket ranges")
+    for a, b in ((case.master, case.o_master), (case.m, case.o_m), (case.v, case.o_v)):
+        assert_bitwise(a.cpu().numpy(), b, "state")
+    pos = case.flat_pos if om == "ag_slot" else np.arange(case.S)
+    assert_bitwise(u16(case.pout)[pos], case.o_p, "param")
+    case.check_canaries(n_probe=4096)
+
+
+def _range_mask(case, b0, b1):
+    """Shard indices of buckets [b0, b1)."""
+    inside = np.zeros(case.S, bool)
+    for b in range(b0, b1):
+        lo = int(case.pl.shard_off[b])
+        inside[lo:lo + int(case.pl.padded_len[b]) // case.w.n_d] = True
+    return inside
+
+
+@pytest.mark.parametrize("numel,cap,n_d,rank,gl,om,b0,b1", [
+    ([70000, 3], 16384, 8, 7, "flat", "ag_slot", 1, 3),
+    ([70000, 3], 16384, 8, 7, "flat", "ag_slot", 4, 5),     # the last bucket alone
+    ([70000, 3], 16384, 8, 7, "flat", "ag_slot", 2, 5),
+    ([1000, 37, 4096, 3], 1500, 4, 3, "compact", "shard", 0, 2),
+    ([8192 * 6], 8192, 8, 2, "flat", "ag_slot", 3, 4),
+    ([50000], 8008, 8, 3, "compact", "ag_slot", 5, 7),
+])
+def test_bucket_range_touches_only_its_slices(numel, cap, n_d, rank, gl, om, b0, b1):
+    case = _edge_case(numel, cap, n_d, rank, gl, om)
+    say(f"  bucket range [{b0}, {b1}) numel={numel} cap={cap} n_d={n_d} {gl} {om}")
+    case.init_state_gpu()
+    case.init_state_oracle()
+    before = [case.master.cpu().numpy(), case.m.cpu().numpy(), case.v.cpu().numpy()]
+    pout0 = u16(case.pout)
+    gout0 = case.gout.cpu().numpy()
+    _step_buckets(case, 1, case.grads_gpu(1), b0, b1)
+    case.step_oracle(1, case.grads_oracle(1))
+    torch.cuda.synchronize()
+    inside = _range_mask(case, b0, b1)
+    assert inside.any()
+    for buf, old, exp in zip((case.master, case.m, case.v), before,
+                             (case.o_master, case.o_m, case.o_v)):
+        got = buf.cpu().numpy()
+        assert_bitwise(got[inside], exp[inside], "state inside the range")
+        assert_bitwise(got[~inside], old[~inside], "state outside the range")
+    g = case.gout.cpu().numpy()
+    assert_bitwise(g[inside], case.o_g[inside], "reduced gradient inside the range")
+    assert_bitwise(g[~inside], gout0[~inside], "reduced gradient outside the range")
+    p = u16(case.pout)
+    pos = case.flat_pos if om == "ag_slot" else np.arange(case.S)
+    assert_bitwise(p[pos[inside]], case.o_p[inside], "param inside the range")
+    untouched = np.ones(p.size, bool)
+    untouched[pos[inside]] = False
+    assert_bitwise(p[untouched], pout0[untouched], "param outside the range")
+
+
+def test_dim0_bucket_ranges_equal_the_whole_step():
+    """Per-parameter layout: tensors stepped in random groups equal one
+    whole-shard step bit for bit (table launches over a tensor range)."""
+    shapes = [((k * 7) % 41 + 1, (k * 5) % 13 + 1) if k % 9 else (64, 64) for k in range(75)]
+    numel = [int(np.prod(s)) for s in shapes]
+    outs = []
+    for split in (False, True):
+        w = workloads.Workload("gpt2s_fsdp2", numel, 0, 4, 2, "flat", "ag_slot", 1, 1,
+                               ("normal", 1e-3), ("normal", 0.02), ("normal", 1e-4),
+                               ("absnormal", 1e-6), rows=[s[0] for s in shapes])
+        case = Case(w)
+        case.init_state_gpu()
+        grads = case.grads_gpu(2)
+        if split:
+            for b0, b1 in _random_ranges(case.L.n_buckets, np.random.default_rng(5)):
+                _step_buckets(case, 2, grads, b0, b1)
+        else:
+            case.step_gpu(2, grads)
+        torch.cuda.synchronize()
+        outs.append([case.master.cpu().numpy(), case.m.cpu().numpy(), case.v.cpu().numpy(),
+                     u16(case.pout), case.gout.cpu().numpy()])
+    for a, b in zip(*outs):
+        assert_bitwise(a, b, "dim0 bucket ranges")
+
+
 # ------------------------------------------------------------------ fp32 contributions
 F32_EDGE = [
     ([1000, 37, 4096, 3], 1500, 4, 3, "flat", "ag_slot"),
