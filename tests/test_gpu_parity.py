@@ -1397,10 +1397,10 @@ def test_hip_graph_capture_of_accumulate_and_step():
 
 def test_hip_graph_capture_of_pack_fused_step_table_step_gather_and_reshard():
     """Every other entry point that launches kernels is capturable too: bucket
-    pack (FLAT contributions), the step with the last micro-batch folded in,
-    a per-parameter (table) step, the parameter gather and a re-cut, captured
-    in one HIP graph; each of several replays equals the same sequence run
-    eagerly, bit for bit."""
+    pack (FLAT contributions), the step in two bucket ranges, the step with
+    the last micro-batch folded in, a per-parameter (table) step, the
+    parameter gather and a re-cut, captured in one HIP graph; each of several
+    replays equals the same sequence run eagerly, bit for bit."""
     shapes = [((k * 7) % 41 + 1, (k * 5) % 13 + 1) if k % 9 else (64, 64) for k in range(40)]
     numel = [int(np.prod(s)) for s in shapes]
     rows = [s[0] for s in shapes]
@@ -1437,8 +1437,10 @@ def test_hip_graph_capture_of_pack_fused_step_table_step_gather_and_reshard():
     def sequence(b, stream=None):
         for q in range(n_d):
             z.zero_bucket_pack(Lb, tens[q], b["flat"][q], stream=stream)
-        z.zero_shard_step(Lb, hp, t, b["flat"], z.GRAD_FLAT, *b["state"][:3], b["pout_b"],
-                          z.OUT_AG_SLOT, stream=stream)
+        half = Lb.n_buckets // 2
+        for b0, b1 in ((half, Lb.n_buckets), (0, half)):
+            z.zero_shard_step_buckets(Lb, hp, t, b0, b1, b["flat"], z.GRAD_FLAT, *b["state"][:3],
+                                      b["pout_b"], z.OUT_AG_SLOT, stream=stream)
         z.zero_shard_step_accumulate(Ld, hp, t, accs, micro, 0.25, z.DTYPE_BF16, z.GRAD_COMPACT,
                                      *b["state"][3:], b["pout_d"], z.OUT_AG_SLOT, stream=stream)
         z.zero_gather_params(Lb, shards, b["full"], stream=stream)
