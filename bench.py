@@ -359,8 +359,9 @@ def aux_kernels(z, synth, workloads, placement):
 
 def next_rows(z, synth, w, L, holder, timed, placement):
     """The rows beyond the bf16 step, measured on llama8b-sized buffers:
-    FSDP2 (dim-0) step, parameter gather, fp32-contribution step, the step
-    with the last micro-batch folded in and the 8 -> 4 rank state re-cut.
+    FSDP2 (dim-0) step, the step in bucket ranges, parameter gathers,
+    re-cuts, fp32-contribution step and the step with the last micro-batch
+    folded in.
     holder[0]: the bench's inputs (released here)."""
     import torch
     dev = torch.device("cuda:0")
@@ -383,6 +384,28 @@ def next_rows(z, synth, w, L, holder, timed, placement):
                                          shard_out, z.OUT_SHARD))
     row("fsdp2_step", "step_vec_kernel", "llama8b_fsdp2: Llama-3-8B per-parameter dim-0 "
         "layout, N_d=8, rank 7, in place", S * (2 * w.n_d + 26), ms)
+    # ZeRO-2 stepping bucket by bucket (as each bucket's Reduce-Scatter
+    # lands): the same update as one call per bucket range, captured in a
+    # HIP graph so that the host's launch rate is not what is timed
+    nb = L.n_buckets
+    for group in (1, 32):
+        def ranges(stream=None, group=group):
+            for b0 in range(0, nb, group):
+                z.zero_shard_step_buckets(L, hp, 6, b0, min(nb, b0 + group), inp.grads,
+                                          z.GRAD_COMPACT, *inp.state, inp.pout, z.OUT_AG_SLOT,
+                                          stream=stream)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                ranges(stream=side)
+        torch.cuda.current_stream().wait_stream(side)
+        ms = timed(graph.replay, reps=5)
+        n_calls = (nb + group - 1) // group
+        row(f"step_buckets_{group}", "step_vec_kernel", f"llama8b step as {n_calls} calls of "
+            f"{group} bucket(s) each (HIP graph)", S * (2 * w.n_d + 26), ms)
+        del graph
     # All-Gather local part: the 8 bf16 shards (the contribution buffers
     # stand in for them) into the 8.03e9-element flat buffer
     ms = timed(lambda: z.zero_gather_params(L, inp.grads, inp.pout))
