@@ -335,44 +335,58 @@ __global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND, GT> A) 
 }
 
 // Many single-bucket regions in one launch (the per-parameter layout, where
-// every tensor is its own bucket): region k covers shard [i0[k], i0[k]+n[k])
-// and flat [f0[k], f0[k]+n[k]).  The work is cut into tiles of blockDim.x*8
-// elements; blocks take tiles grid-stride and find a tile's region by binary
-// search over the tile prefix sums, so a 38.6M-element embedding and
-// 96-element norm slices share one launch without idle blocks.  Regions whose
-// addresses are not all 16-byte aligned (bit clear in `vec`) run element by
-// element.  A launch takes up to 64 regions for the compile-time rank counts
-// and 32 for the runtime-N_d instantiation, whose pointer arrays are larger:
-// the kernel arguments stay under 4 KB.
+// every tensor is its own bucket).  The regions of one launch are
+// consecutive non-empty slices, so they tile one shard range: region k
+// covers shard [i_base + e0[k], i_base + e0[k+1]) and flat [f0[k], f0[k] +
+// its length).  The work is cut into tiles of blockDim.x*8 elements; blocks
+// take tiles grid-stride and find a tile's region by binary search over the
+// tile prefix sums, so a 38.6M-element embedding and 96-element norm slices
+// share one launch without idle blocks.  Regions whose shard or flat start
+// is not a multiple of 8 (or every region, when a base pointer is not
+// 16-byte aligned) run element by element.  20 bytes per region: a launch
+// takes as many regions as fit next to the kernel's other arguments in
+// 4 KB (191 for bf16 contributions at N_d = 8).
 template <int CAP>
 struct TableT {
-  int64_t i0[CAP], f0[CAP], n[CAP];
-  int64_t tile0[CAP + 1];  // first tile of each region; tile0[count] = total
-  uint64_t vec;
+  int64_t i_base;
+  int64_t e0[CAP + 1];
+  int64_t f0[CAP];
+  uint32_t tile0[CAP + 1];  // first tile of each region; tile0[count] = total
   int32_t count;
+  int32_t vec_ok;  // base pointers 16-byte aligned and the vector path allowed
 };
-template <int ND>
-using TableFor = TableT<(ND > 0 ? 64 : 32)>;
-using HostTable = TableT<64>;
+constexpr int kHostTableCap = 192;
+// tiles per launch stay below 2^30, so that tile + gridDim.x fits 32 bits
+constexpr int64_t kMaxTableTiles = (int64_t)1 << 30;
+
+template <int ND, int GT>
+constexpr int table_cap_of() {
+  constexpr int64_t room = (4096 - (int64_t)sizeof(ArgsFor<ND, GT>) - 40) / 20;
+  return (int)(room < kHostTableCap ? room : kHostTableCap);
+}
+template <int ND, int GT>
+using TableFor = TableT<table_cap_of<ND, GT>()>;
+using HostTable = TableT<kHostTableCap>;
 
 template <int ND, int GROUP, bool NT, int GT>
 __global__ void __launch_bounds__(256) step_table_kernel(const ArgsFor<ND, GT> A,
-                                                         const TableFor<ND> T) {
+                                                         const TableFor<ND, GT> T) {
   const int64_t span = (int64_t)blockDim.x << 3;
-  const int64_t total = T.tile0[T.count];
-  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+  const uint32_t total = T.tile0[T.count];
+  for (uint32_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
     int lo = 0, hi = T.count;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (T.tile0[mid] <= tile) lo = mid;
       else hi = mid;
     }
-    const int64_t n = T.n[lo];
-    const int64_t e0 = (tile - T.tile0[lo]) * span + ((int64_t)threadIdx.x << 3);
+    const int64_t r0 = T.i_base + T.e0[lo], f0 = T.f0[lo];
+    const int64_t n = T.e0[lo + 1] - T.e0[lo];
+    const int64_t e0 = (int64_t)(tile - T.tile0[lo]) * span + ((int64_t)threadIdx.x << 3);
     if (e0 >= n) continue;
-    const int64_t i = T.i0[lo] + e0, f = T.f0[lo] + e0;
+    const int64_t i = r0 + e0, f = f0 + e0;
     const int64_t gi = A.flat_grad ? f : i, oi = A.slot_out ? f : i;
-    if (((T.vec >> lo) & 1ull) && e0 + 8 <= n) {
+    if (T.vec_ok && ((r0 | f0) & 7) == 0 && e0 + 8 <= n) {
       step8<ND, GROUP, NT, GT>(A, i, gi, oi);
     } else {
       const int64_t m = n - e0 < 8 ? n - e0 : 8;
@@ -472,8 +486,27 @@ struct Work {
   int blocks, threads;
 };
 
-bool static_nd(int nd) { return nd == 2 || nd == 4 || nd == 8 || nd == 16 || nd == 32 || nd == 64; }
-int table_cap(int nd) { return static_nd(nd) ? 64 : 32; }
+template <int GT>
+int table_cap_gt(int nd) {
+  switch (nd) {
+    case 2: return table_cap_of<2, GT>();
+    case 4: return table_cap_of<4, GT>();
+    case 8: return table_cap_of<8, GT>();
+    case 16: return table_cap_of<16, GT>();
+    case 32: return table_cap_of<32, GT>();
+    case 64: return table_cap_of<64, GT>();
+    default: return table_cap_of<0, GT>();
+  }
+}
+// Regions per table launch for this rank count and contribution type.
+int table_cap(int nd, int gt) {
+  switch (gt) {
+    case GT_F32: return table_cap_gt<GT_F32>(nd);
+    case GT_ACC_BF16: return table_cap_gt<GT_ACC_BF16>(nd);
+    case GT_ACC_F32: return table_cap_gt<GT_ACC_F32>(nd);
+    default: return table_cap_gt<GT_BF16>(nd);
+  }
+}
 
 template <int ND, int GT, int KIND, bool NT>
 int launch_nt(const Call& c, const Work& w, hipStream_t s) {
@@ -484,19 +517,19 @@ int launch_nt(const Call& c, const Work& w, hipStream_t s) {
   constexpr int GMAX = fused(GT) ? 8 : 16;
   constexpr int GROUP = ND > GMAX ? GMAX : (ND > 1 ? ND - 1 : 1);
   if constexpr (KIND == K_TABLE) {
-    using Tab = TableFor<ND>;
+    using Tab = TableFor<ND, GT>;
     static_assert(sizeof(ArgsFor<ND, GT>) + sizeof(Tab) <= 4096, "kernel arguments");
     Tab T;
     const int n = w.tab->count;
-    for (int k = 0; k < n; ++k) {
-      T.i0[k] = w.tab->i0[k];
-      T.f0[k] = w.tab->f0[k];
-      T.n[k] = w.tab->n[k];
+    if (n < 1 || n > table_cap_of<ND, GT>()) return ZERO_EINVAL;  // planner invariant
+    T.i_base = w.tab->i_base;
+    for (int k = 0; k < n; ++k) T.f0[k] = w.tab->f0[k];
+    for (int k = 0; k <= n; ++k) {
+      T.e0[k] = w.tab->e0[k];
       T.tile0[k] = w.tab->tile0[k];
     }
-    T.tile0[n] = w.tab->tile0[n];
-    T.vec = w.tab->vec;
     T.count = n;
+    T.vec_ok = w.tab->vec_ok;
     hipLaunchKernelGGL((step_table_kernel<ND, GROUP, NT, GT>), dim3(w.blocks), dim3(w.threads), 0,
                        s, A, T);
   } else {
@@ -649,13 +682,15 @@ int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int3
 
   if (map && !L->fixed()) {
     // per-parameter (dim-0) layout: every tensor is its own bucket; the
-    // non-empty slices go to table launches of up to table_cap(nd) regions
+    // non-empty slices, consecutive in the shard, go to table launches of
+    // up to table_cap(nd, gt) regions
     const int64_t span_e = (int64_t)threads * 8;
-    const int tcap = table_cap(nd);
+    for (int64_t b = b0; b < b1; ++b)
+      if ((L->bucket_slice(b) + span_e - 1) / span_e >= kMaxTableTiles) return ZERO_ERANGE;
+    const int tcap = table_cap(nd, c.gt);
     HostTable T;
     T.count = 0;
-    T.vec = 0;
-    T.tile0[0] = 0;
+    T.vec_ok = allow_vec ? 1 : 0;
     auto flush = [&]() -> int {
       if (T.count == 0) return ZERO_OK;
       const int64_t total = T.tile0[T.count];
@@ -663,24 +698,31 @@ int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int3
       const Work w{nullptr, &T, blocks, threads};
       const int rc = dispatch<K_TABLE>(c, w, stream);
       T.count = 0;
-      T.vec = 0;
       return rc;
     };
     for (int64_t b = b0; b < b1; ++b) {
       const int64_t sl = L->bucket_slice(b);
       if (sl == 0) continue;
       const int64_t i0 = L->bucket_shard_off(b), f0 = L->bucket_padded_off(b) + r * sl;
+      const int64_t tiles = (sl + span_e - 1) / span_e;
+      if (T.count > 0 && (i0 != T.i_base + T.e0[T.count] ||
+                          (int64_t)T.tile0[T.count] + tiles >= kMaxTableTiles)) {
+        const int rc = flush();
+        if (rc != ZERO_OK) return rc;
+      }
+      if (T.count == 0) {
+        T.i_base = i0;
+        T.e0[0] = 0;
+        T.tile0[0] = 0;
+      }
       const int k = T.count;
-      T.i0[k] = i0;
       T.f0[k] = f0;
-      T.n[k] = sl;
-      if (allow_vec && i0 % 8 == 0 && f0 % 8 == 0) T.vec |= 1ull << k;
-      T.tile0[k + 1] = T.tile0[k] + (sl + span_e - 1) / span_e;
+      T.e0[k + 1] = T.e0[k] + sl;
+      T.tile0[k + 1] = T.tile0[k] + (uint32_t)tiles;
       T.count = k + 1;
       if (T.count == tcap) {
         const int rc = flush();
         if (rc != ZERO_OK) return rc;
-        T.tile0[0] = 0;
       }
     }
     return flush();

@@ -22,8 +22,8 @@
  * local write of the All-Gather (the rank's bf16 slice into its slot of the
  * gathered buffer), in one streaming pass over the shard (one kernel launch
  * per call for a bucketed layout with 16-byte aligned buffers; per-parameter
- * layouts take one launch per 64 tensors, or per 32 when n_d is not one of
- * 2, 4, 8, 16, 32, 64).  No collective is issued.
+ * layouts take one launch per 143 to 192 tensors, or per 92 when n_d is not
+ * one of 2, 4, 8, 16, 32, 64).  No collective is issued.
  *
  * Conventions for every entry point:
  *   - Returns ZERO_OK or a negative zero_status.  Arguments are validated on

@@ -697,14 +697,16 @@ def test_bucket_range_touches_only_its_slices(numel, cap, n_d, rank, gl, om, b0,
     assert_bitwise(p[untouched], pout0[untouched], "param outside the range")
 
 
-def test_dim0_bucket_ranges_equal_the_whole_step():
+@pytest.mark.parametrize("gl,om", [("flat", "ag_slot"), ("compact", "shard")])
+def test_dim0_bucket_ranges_equal_the_whole_step(gl, om):
     """Per-parameter layout: tensors stepped in random groups equal one
-    whole-shard step bit for bit (table launches over a tensor range)."""
+    whole-shard step bit for bit (table launches over a tensor range; one
+    plain shard range without flat addressing)."""
     shapes = [((k * 7) % 41 + 1, (k * 5) % 13 + 1) if k % 9 else (64, 64) for k in range(75)]
     numel = [int(np.prod(s)) for s in shapes]
     outs = []
     for split in (False, True):
-        w = workloads.Workload("gpt2s_fsdp2", numel, 0, 4, 2, "flat", "ag_slot", 1, 1,
+        w = workloads.Workload("gpt2s_fsdp2", numel, 0, 4, 2, gl, om, 1, 1,
                                ("normal", 1e-3), ("normal", 0.02), ("normal", 1e-4),
                                ("absnormal", 1e-6), rows=[s[0] for s in shapes])
         case = Case(w)
@@ -1227,9 +1229,17 @@ DIM0_EDGE = [
      4, 3, "flat", "ag_slot"),
     ([((k * 7) % 41 + 1, (k * 5) % 13 + 1) if k % 9 else (64, 64) for k in range(75)],
      8, 0, "compact", "ag_slot"),
-    # runtime rank count: table launches of 32 slices
+    # runtime rank count: a table launch holds 92 slices
     ([((k * 7) % 41 + 1, (k * 5) % 13 + 1) if k % 9 else (64, 64) for k in range(75)],
      3, 2, "flat", "ag_slot"),
+    ([((k * 7) % 41 + 1, (k * 5) % 13 + 1) if k % 9 else (64, 64) for k in range(230)],
+     3, 1, "flat", "ag_slot"),
+    # 400 tensors, 8 of them empty, many with only padding rows on rank 7:
+    # three table launches of up to 191 slices
+    ([(0, 5) if k % 50 == 3 else ((k * 11) % 37 + 1, (k * 3) % 7 + 1) if k % 5 else (2, 24)
+      for k in range(400)], 8, 7, "flat", "ag_slot"),
+    ([(0, 5) if k % 50 == 3 else ((k * 11) % 37 + 1, (k * 3) % 7 + 1) if k % 5 else (2, 24)
+      for k in range(400)], 4, 1, "compact", "ag_slot"),
 ]
 
 
