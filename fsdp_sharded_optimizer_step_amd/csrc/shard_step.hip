@@ -120,18 +120,23 @@ struct Raw8<GT_F32> {
   f32x4 lo, hi;
 };
 
-template <int GT, bool NT, class Args>
+// Cache policy of a launch (bit set: non-temporal): the contribution loads,
+// the master / m / v loads, and every store.
+enum : int { NT_CONTRIB = 1, NT_STATE = 2, NT_STORE = 4 };
+
+template <int GT, int NT, class Args>
 __device__ __forceinline__ Raw8<GT> load8(const Args& A, int q, int64_t gi) {
+  constexpr bool nt = (NT & NT_CONTRIB) != 0;
   Raw8<GT> r;
   if constexpr (GT == GT_BF16) {
-    r.w = ld_stream<NT>((const u32x4*)((const uint16_t*)A.g[q] + gi));
+    r.w = ld_stream<nt>((const u32x4*)((const uint16_t*)A.g[q] + gi));
   } else if constexpr (GT == GT_F32) {
-    r.lo = ld_stream<NT>((const f32x4*)((const float*)A.g[q] + gi));
-    r.hi = ld_stream<NT>((const f32x4*)((const float*)A.g[q] + gi + 4));
+    r.lo = ld_stream<nt>((const f32x4*)((const float*)A.g[q] + gi));
+    r.hi = ld_stream<nt>((const f32x4*)((const float*)A.g[q] + gi + 4));
   } else {
-    r.lo = ld_stream<NT>((const f32x4*)(A.a[q] + gi));
-    r.hi = ld_stream<NT>((const f32x4*)(A.a[q] + gi + 4));
-    r.w = ld_stream<NT>((const u32x4*)((const uint16_t*)A.g[q] + gi));
+    r.lo = ld_stream<nt>((const f32x4*)(A.a[q] + gi));
+    r.hi = ld_stream<nt>((const f32x4*)(A.a[q] + gi + 4));
+    r.w = ld_stream<nt>((const u32x4*)((const uint16_t*)A.g[q] + gi));
   }
   return r;
 }
@@ -188,7 +193,7 @@ __device__ __forceinline__ float load_one(const Args& A, int q, int64_t gi) {
 // The loads of up to GROUP ranks are issued before their adds.
 // The fused contributions at large N_d keep the group loop rolled: fully
 // unrolled, the scheduler hoists loads of later groups and spills.
-template <int ND, int GROUP, bool NT, int GT>
+template <int ND, int GROUP, int NT, int GT>
 __device__ __forceinline__ void reduce8(float acc[8], const ArgsFor<ND, GT>& A, int64_t gi) {
   widen8<GT>(acc, load8<GT, NT>(A, 0, gi), A);
   if constexpr (fused(GT) && ND > 16) {
@@ -217,7 +222,7 @@ __device__ __forceinline__ void reduce8(float acc[8], const ArgsFor<ND, GT>& A, 
 }
 
 // Runtime rank count.
-template <bool NT, int GT>
+template <int NT, int GT>
 __device__ __forceinline__ void reduce8_dyn(float acc[8], const ArgsFor<0, GT>& A, int64_t gi) {
   widen8<GT>(acc, load8<GT, NT>(A, 0, gi), A);
   for (int q = 1; q < A.nd; ++q) add8<GT>(acc, load8<GT, NT>(A, q, gi), A);
@@ -254,7 +259,7 @@ __device__ __forceinline__ void step_one(const Args& A, int64_t e, bool map) {
 
 // 8 consecutive elements with 128-bit accesses: shard index i, contribution
 // index gi, output index oi (all multiples of 8 on 16-byte aligned bases).
-template <int ND, int GROUP, bool NT, int GT>
+template <int ND, int GROUP, int NT, int GT>
 __device__ __forceinline__ void step8(const ArgsFor<ND, GT>& A, int64_t i, int64_t gi,
                                       int64_t oi) {
   float acc[8];
@@ -263,12 +268,13 @@ __device__ __forceinline__ void step8(const ArgsFor<ND, GT>& A, int64_t i, int64
   else
     reduce8_dyn<NT, GT>(acc, A, gi);
 
-  const f32x4 th0 = ld_stream<NT>((const f32x4*)(A.master + i));
-  const f32x4 th1 = ld_stream<NT>((const f32x4*)(A.master + i + 4));
-  const f32x4 m0 = ld_stream<NT>((const f32x4*)(A.m + i));
-  const f32x4 m1 = ld_stream<NT>((const f32x4*)(A.m + i + 4));
-  const f32x4 v0 = ld_stream<NT>((const f32x4*)(A.v + i));
-  const f32x4 v1 = ld_stream<NT>((const f32x4*)(A.v + i + 4));
+  constexpr bool nts = (NT & NT_STATE) != 0, ntw = (NT & NT_STORE) != 0;
+  const f32x4 th0 = ld_stream<nts>((const f32x4*)(A.master + i));
+  const f32x4 th1 = ld_stream<nts>((const f32x4*)(A.master + i + 4));
+  const f32x4 m0 = ld_stream<nts>((const f32x4*)(A.m + i));
+  const f32x4 m1 = ld_stream<nts>((const f32x4*)(A.m + i + 4));
+  const f32x4 v0 = ld_stream<nts>((const f32x4*)(A.v + i));
+  const f32x4 v1 = ld_stream<nts>((const f32x4*)(A.v + i + 4));
   float th[8] = {th0.x, th0.y, th0.z, th0.w, th1.x, th1.y, th1.z, th1.w};
   float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
   float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -278,18 +284,18 @@ __device__ __forceinline__ void step8(const ArgsFor<ND, GT>& A, int64_t i, int64
     g[k] = average<((ND & (ND - 1)) == 0 ? ND : 0)>(acc[k], A);
     adamw(g[k], th[k], mm[k], vv[k], A.k);
   }
-  st_stream<NT>((f32x4*)(A.master + i), f32x4{th[0], th[1], th[2], th[3]});
-  st_stream<NT>((f32x4*)(A.master + i + 4), f32x4{th[4], th[5], th[6], th[7]});
-  st_stream<NT>((f32x4*)(A.m + i), f32x4{mm[0], mm[1], mm[2], mm[3]});
-  st_stream<NT>((f32x4*)(A.m + i + 4), f32x4{mm[4], mm[5], mm[6], mm[7]});
-  st_stream<NT>((f32x4*)(A.v + i), f32x4{vv[0], vv[1], vv[2], vv[3]});
-  st_stream<NT>((f32x4*)(A.v + i + 4), f32x4{vv[4], vv[5], vv[6], vv[7]});
-  st_stream<NT>((u32x4*)(A.pout + oi),
+  st_stream<ntw>((f32x4*)(A.master + i), f32x4{th[0], th[1], th[2], th[3]});
+  st_stream<ntw>((f32x4*)(A.master + i + 4), f32x4{th[4], th[5], th[6], th[7]});
+  st_stream<ntw>((f32x4*)(A.m + i), f32x4{mm[0], mm[1], mm[2], mm[3]});
+  st_stream<ntw>((f32x4*)(A.m + i + 4), f32x4{mm[4], mm[5], mm[6], mm[7]});
+  st_stream<ntw>((f32x4*)(A.v + i), f32x4{vv[0], vv[1], vv[2], vv[3]});
+  st_stream<ntw>((f32x4*)(A.v + i + 4), f32x4{vv[4], vv[5], vv[6], vv[7]});
+  st_stream<ntw>((u32x4*)(A.pout + oi),
                 u32x4{bf16_pack2(th[0], th[1]), bf16_pack2(th[2], th[3]),
                       bf16_pack2(th[4], th[5]), bf16_pack2(th[6], th[7])});
   if (A.gout) {
-    st_stream<NT>((f32x4*)(A.gout + i), f32x4{g[0], g[1], g[2], g[3]});
-    st_stream<NT>((f32x4*)(A.gout + i + 4), f32x4{g[4], g[5], g[6], g[7]});
+    st_stream<ntw>((f32x4*)(A.gout + i), f32x4{g[0], g[1], g[2], g[3]});
+    st_stream<ntw>((f32x4*)(A.gout + i + 4), f32x4{g[4], g[5], g[6], g[7]});
   }
 }
 
@@ -298,7 +304,7 @@ __device__ __forceinline__ void step8(const ArgsFor<ND, GT>& A, int64_t i, int64
 // flat0 % 8 == 0 and (part 0 is one bucket, or seg % 8 == 0 and
 // pstride % 8 == 0), and if part 1 exists n0 % 8 == 0 and flat1 % 8 == 0, so
 // that no vector straddles a bucket and every vector address is aligned.
-template <int ND, bool MAP, int GROUP, bool NT, int GT>
+template <int ND, bool MAP, int GROUP, int NT, int GT>
 __global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND, GT> A) {
   const int64_t n = A.reg.n;
   const int64_t nv0 = A.reg.n0 >> 3;
@@ -368,7 +374,7 @@ template <int ND, int GT>
 using TableFor = TableT<table_cap_of<ND, GT>()>;
 using HostTable = TableT<kHostTableCap>;
 
-template <int ND, int GROUP, bool NT, int GT>
+template <int ND, int GROUP, int NT, int GT>
 __global__ void __launch_bounds__(256) step_table_kernel(const ArgsFor<ND, GT> A,
                                                          const TableFor<ND, GT> T) {
   const int64_t span = (int64_t)blockDim.x << 3;
@@ -464,6 +470,13 @@ int cu_count() {
 //   accumulator + last micro-batch: ordinary accesses, one 256-thread block
 //     per CU (12.6 ms against 13.2 with two).
 constexpr bool read_dominated(int nd, int gt) { return nd * contrib_bytes(gt) >= 64; }
+// Measured on the tuned llama8b / llama70b buffers (mix kernel and step):
+// bf16 contributions, one 16-byte load per lane and 8 elements, stream
+// best non-temporal (+2 % at N_d = 8 and 64, +8 % at 15.6M elements), and
+// non-temporal stores add a little.  Loads that fetch a cache line in two
+// halves (fp32 contributions, accumulators, the fp32 state: two 16-byte
+// loads per lane) lose 5-10 % when non-temporal, so they stay ordinary.
+constexpr int cache_policy(int gt) { return gt == GT_BF16 ? NT_CONTRIB | NT_STORE : 0; }
 struct Policy {
   int blocks_per_cu, threads;
 };
@@ -508,7 +521,7 @@ int table_cap(int nd, int gt) {
   }
 }
 
-template <int ND, int GT, int KIND, bool NT>
+template <int ND, int GT, int KIND, int NT>
 int launch_nt(const Call& c, const Work& w, hipStream_t s) {
   ArgsFor<ND, GT> A;
   fill_args(A, c, w.reg ? *w.reg : Region{0, 0, 0, 1, 0, 0, 0});
@@ -541,11 +554,7 @@ int launch_nt(const Call& c, const Work& w, hipStream_t s) {
 
 template <int ND, int GT, int KIND>
 int launch(const Call& c, const Work& w, hipStream_t s) {
-  if constexpr (ND > 0)
-    return launch_nt<ND, GT, KIND, read_dominated(ND, GT)>(c, w, s);
-  else
-    return read_dominated(c.nd, GT) ? launch_nt<0, GT, KIND, true>(c, w, s)
-                                    : launch_nt<0, GT, KIND, false>(c, w, s);
+  return launch_nt<ND, GT, KIND, cache_policy(GT)>(c, w, s);
 }
 
 template <int GT, int KIND>

@@ -29,7 +29,9 @@ def _load():
 
 def stream_ceiling(grads, state, out, n: int, reps: int = 5):
     """Best bandwidth (GB/s of 2*N_d + 26 bytes per element) of the same-mix
-    kernel over a few launch shapes, on the given (scratch) buffers."""
+    kernel over a few launch shapes and cache policies (non-temporal: none,
+    contribution loads, contribution loads and stores, everything), on the
+    given (scratch) buffers."""
     import torch
     lib = _load()
     nd = len(grads)
@@ -40,8 +42,8 @@ def stream_ceiling(grads, state, out, n: int, reps: int = 5):
     stream = torch.cuda.current_stream()
     best = (0.0, None)
     for bpc in (1, 2, 4):
-        for nt in (0, 1):
-            args = (g, nd, s, out.data_ptr(), n, cus * bpc, nt, stream.cuda_stream)
+        for pol in (0, 1, 5, 7):
+            args = (g, nd, s, out.data_ptr(), n, cus * bpc, pol, stream.cuda_stream)
             if lib.stream_ceiling_launch(*args) != 0:
                 raise RuntimeError("stream_ceiling_launch failed")
             e0 = torch.cuda.Event(enable_timing=True)
@@ -54,7 +56,7 @@ def stream_ceiling(grads, state, out, n: int, reps: int = 5):
             ms = e0.elapsed_time(e1) / reps
             gbps = n * (2 * nd + 26) / (ms * 1e-3) / 1e9
             if gbps > best[0]:
-                best = (gbps, {"blocks_per_cu": bpc, "nontemporal": bool(nt), "ms": ms})
+                best = (gbps, {"blocks_per_cu": bpc, "nontemporal_policy": pol, "ms": ms})
     return best
 
 

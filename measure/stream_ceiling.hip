@@ -35,27 +35,40 @@ __device__ __forceinline__ void st(u32x4* p, u32x4 v) {
   else *p = v;
 }
 
-template <int ND, bool NT>
+// POL: cache policy bits (set: non-temporal) 1 = contribution loads,
+// 2 = state loads, 4 = stores.
+template <int ND, int POL>
 __global__ void __launch_bounds__(256) mix_kernel(const MixArgs a) {
+  constexpr bool gn = (POL & 1) != 0, sn = (POL & 2) != 0, wn = (POL & 4) != 0;
   const int64_t T = (int64_t)gridDim.x * blockDim.x;
   const int nd = ND > 0 ? ND : a.nd;
   for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < a.nvec; v += T) {
-    u32x4 acc = ld<NT>(a.g[0] + v);
+    u32x4 acc = ld<gn>(a.g[0] + v);
 #pragma unroll
     for (int q = 1; q < (ND > 0 ? ND : kMaxRanks); ++q)
-      if (q < nd) acc += ld<NT>(a.g[q] + v);
+      if (q < nd) acc += ld<gn>(a.g[q] + v);
     u32x4 x[6];
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-      x[2 * k] = ld<NT>(a.s[k] + 2 * v);
-      x[2 * k + 1] = ld<NT>(a.s[k] + 2 * v + 1);
+      x[2 * k] = ld<sn>(a.s[k] + 2 * v);
+      x[2 * k + 1] = ld<sn>(a.s[k] + 2 * v + 1);
     }
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-      st<NT>(a.s[k] + 2 * v, x[2 * k] + acc);
-      st<NT>(a.s[k] + 2 * v + 1, x[2 * k + 1] ^ acc);
+      st<wn>(a.s[k] + 2 * v, x[2 * k] + acc);
+      st<wn>(a.s[k] + 2 * v + 1, x[2 * k + 1] ^ acc);
     }
-    st<NT>(a.p + v, acc);
+    st<wn>(a.p + v, acc);
+  }
+}
+
+template <int ND>
+void launch_mix(int pol, const MixArgs& a, int blocks, hipStream_t stream) {
+  switch (pol) {
+    case 1: hipLaunchKernelGGL((mix_kernel<ND, 1>), dim3(blocks), dim3(256), 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((mix_kernel<ND, 5>), dim3(blocks), dim3(256), 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((mix_kernel<ND, 7>), dim3(blocks), dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((mix_kernel<ND, 0>), dim3(blocks), dim3(256), 0, stream, a);
   }
 }
 
@@ -89,11 +102,13 @@ extern "C" {
 
 // grads: host array of nd device pointers to n bf16 values each; state: 3
 // device pointers to n floats; out: n bf16 values.  n must be a multiple of
-// 8 and every pointer 16-byte aligned.  Returns 0, -1 on bad arguments, -2
-// on a launch failure.
+// 8 and every pointer 16-byte aligned.  pol: cache policy, one of 0, 1, 5, 7
+// (bits: 1 contribution loads, 2 state loads, 4 stores non-temporal).
+// Returns 0, -1 on bad arguments, -2 on a launch failure.
 int stream_ceiling_launch(const void* const* grads, int32_t nd, void* const* state, void* out,
-                          int64_t n, int32_t blocks, int32_t nt, hipStream_t stream) {
-  if (nd < 1 || nd > kMaxRanks || n < 0 || n % 8 != 0 || blocks < 1 || !grads || !state || !out)
+                          int64_t n, int32_t blocks, int32_t pol, hipStream_t stream) {
+  if (nd < 1 || nd > kMaxRanks || n < 0 || n % 8 != 0 || blocks < 1 || !grads || !state || !out ||
+      (pol != 0 && pol != 1 && pol != 5 && pol != 7))
     return -1;
   MixArgs a;
   for (int q = 0; q < kMaxRanks; ++q) a.g[q] = q < nd ? (const u32x4*)grads[q] : nullptr;
@@ -106,16 +121,9 @@ int stream_ceiling_launch(const void* const* grads, int32_t nd, void* const* sta
   for (int k = 0; k < 3; ++k)
     if (!state[k] || ((uintptr_t)state[k] & 15u)) return -1;
   if ((uintptr_t)out & 15u) return -1;
-  if (nd == 8) {
-    if (nt) hipLaunchKernelGGL((mix_kernel<8, true>), dim3(blocks), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((mix_kernel<8, false>), dim3(blocks), dim3(256), 0, stream, a);
-  } else if (nd == 64) {
-    if (nt) hipLaunchKernelGGL((mix_kernel<64, true>), dim3(blocks), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((mix_kernel<64, false>), dim3(blocks), dim3(256), 0, stream, a);
-  } else {
-    if (nt) hipLaunchKernelGGL((mix_kernel<0, true>), dim3(blocks), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((mix_kernel<0, false>), dim3(blocks), dim3(256), 0, stream, a);
-  }
+  if (nd == 8) launch_mix<8>(pol, a, blocks, stream);
+  else if (nd == 64) launch_mix<64>(pol, a, blocks, stream);
+  else launch_mix<0>(pol, a, blocks, stream);
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
