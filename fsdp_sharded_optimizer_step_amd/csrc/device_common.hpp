@@ -9,14 +9,15 @@
 
 namespace zs {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Streaming accesses: every byte is touched exactly once per call.  NT
-// selects the non-temporal cache hint.  Measured on MI355X, it helps the
-// read-dominated step at large N_d and costs bandwidth on the mixed
-// read/write streams (small N_d, accumulate, pack), so it is a per-kernel
-// choice.
+// selects the non-temporal cache hint.  Measured on MI355X, it pays only
+// where each cache line is fetched by a single instruction of a wave; where
+// a lane reads two halves of a line with two instructions the line is
+// fetched twice.  It is chosen per kernel and per stream.
 template <bool NT, class T>
 __device__ __forceinline__ T ld_stream(const T* p) {
   if constexpr (NT)

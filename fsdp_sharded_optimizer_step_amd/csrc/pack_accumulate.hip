@@ -8,10 +8,10 @@
 // parameters of a unit are flattened and concatenated into one flat buffer
 // that is split evenly, padding included.
 //
-// Both kernels are HBM streams: 128-bit loads/stores, no LDS.  Pack moves 4
-// bytes per element (2 per pad element) in tiles; accumulate moves 6
-// (overwrite), 10 (add) or 8 (add, emit bf16, no fp32 store) bytes in a
-// grid-stride loop.
+// Both kernels are HBM streams with whole cache lines per instruction, no
+// LDS.  Pack moves 4 bytes per element (2 per pad element) in tiles;
+// accumulate moves 6 (overwrite), 10 (add) or 8 (add, emit bf16, no fp32
+// store) bytes in a grid-stride loop over 512-element chunks.
 #include <algorithm>
 #include <cstdint>
 #include <vector>
@@ -94,39 +94,52 @@ __global__ void __launch_bounds__(kPackThreads) pack_kernel(const PackArgs A) {
 }
 
 // ------------------------------------------------------------------ accumulate
-template <bool NT>
+// Measured on accum1p3b-sized buffers (162.5M elements), every cache policy
+// and 1-16 blocks per CU: non-temporal everything and 4 blocks of 256
+// threads per CU are best for all three call kinds (overwrite 0.166 ms,
+// add 0.265 ms, add + emit bf16 without store 0.206 ms).
+constexpr int kAccPolicy = 7;
+constexpr int kAccBlocksPerCu = 4;
+// Grid-stride over chunks of 512 elements per wave; lane l takes the
+// 4-element pieces at 4l and 256 + 4l, so that every load and store
+// instruction of a wave covers whole cache lines (8-byte bf16, 16-byte fp32
+// accesses).  POL bits (set: non-temporal): 1 gradient loads, 2 accumulator
+// loads, 4 stores.  The elements after the last full chunk go one per
+// thread.
+template <int POL>
 __global__ void __launch_bounds__(256) accum_vec_kernel(float* acc, const uint16_t* g, int64_t n,
                                                         float scale, uint32_t flags,
                                                         uint16_t* out) {
+  constexpr bool ng = (POL & 1) != 0, na = (POL & 2) != 0, nw = (POL & 4) != 0;
   const bool overwrite = flags & ZERO_ACC_OVERWRITE;
   const bool emit = flags & ZERO_ACC_EMIT_BF16;
   const bool store = !(flags & ZERO_ACC_NO_STORE);
-  const int64_t nv = n >> 3;
+  const int64_t nchunk = n >> 9;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t T = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t k = tid; k < nv; k += T) {
-    const int64_t i = k << 3;
-    const u32x4 w = ld_stream<NT>((const u32x4*)(g + i));
-    float a[8] = {scale * bf16_lo(w.x), scale * bf16_hi(w.x), scale * bf16_lo(w.y),
-                  scale * bf16_hi(w.y), scale * bf16_lo(w.z), scale * bf16_hi(w.z),
-                  scale * bf16_lo(w.w), scale * bf16_hi(w.w)};
+  for (int64_t c = tid >> 6; c < nchunk; c += T >> 6) {
+    const int64_t ea = (c << 9) + ((threadIdx.x & 63) << 2), eb = ea + 256;
+    const u32x2 wa = ld_stream<ng>((const u32x2*)(g + ea));
+    const u32x2 wb = ld_stream<ng>((const u32x2*)(g + eb));
+    float a[8] = {scale * bf16_lo(wa.x), scale * bf16_hi(wa.x), scale * bf16_lo(wa.y),
+                  scale * bf16_hi(wa.y), scale * bf16_lo(wb.x), scale * bf16_hi(wb.x),
+                  scale * bf16_lo(wb.y), scale * bf16_hi(wb.y)};
     if (!overwrite) {
-      const f32x4 a0 = ld_stream<NT>((const f32x4*)(acc + i));
-      const f32x4 a1 = ld_stream<NT>((const f32x4*)(acc + i + 4));
+      const f32x4 a0 = ld_stream<na>((const f32x4*)(acc + ea));
+      const f32x4 a1 = ld_stream<na>((const f32x4*)(acc + eb));
       a[0] = a0.x + a[0]; a[1] = a0.y + a[1]; a[2] = a0.z + a[2]; a[3] = a0.w + a[3];
       a[4] = a1.x + a[4]; a[5] = a1.y + a[5]; a[6] = a1.z + a[6]; a[7] = a1.w + a[7];
     }
     if (store) {
-      st_stream<NT>((f32x4*)(acc + i), f32x4{a[0], a[1], a[2], a[3]});
-      st_stream<NT>((f32x4*)(acc + i + 4), f32x4{a[4], a[5], a[6], a[7]});
+      st_stream<nw>((f32x4*)(acc + ea), f32x4{a[0], a[1], a[2], a[3]});
+      st_stream<nw>((f32x4*)(acc + eb), f32x4{a[4], a[5], a[6], a[7]});
     }
-    if (emit)
-      st_stream<NT>((u32x4*)(out + i), u32x4{bf16_pack2(a[0], a[1]), bf16_pack2(a[2], a[3]),
-                                         bf16_pack2(a[4], a[5]), bf16_pack2(a[6], a[7])});
+    if (emit) {
+      st_stream<nw>((u32x2*)(out + ea), u32x2{bf16_pack2(a[0], a[1]), bf16_pack2(a[2], a[3])});
+      st_stream<nw>((u32x2*)(out + eb), u32x2{bf16_pack2(a[4], a[5]), bf16_pack2(a[6], a[7])});
+    }
   }
-  const int64_t tail0 = nv << 3;
-  if (tid < n - tail0) {
-    const int64_t i = tail0 + tid;
+  for (int64_t i = (nchunk << 9) + tid; i < n; i += T) {
     const float c = scale * bf16_one(g[i]);
     const float a = overwrite ? c : acc[i] + c;
     if (store) acc[i] = a;
@@ -249,20 +262,15 @@ int zero_grad_accumulate(float* acc, const uint16_t* grad, int64_t n, float scal
   if (overlap(grad, 2 * n, acc, 4 * n) || (emit && (overlap(bf16_out, 2 * n, grad, 2 * n) ||
                                                    overlap(bf16_out, 2 * n, acc, 4 * n))))
     return ZERO_EOVERLAP;
-  // Launch policy, measured on MI355X for the three call kinds: 4 blocks of
-  // 256 threads per CU; non-temporal accesses only for the read-dominated
-  // last call (add, emit bf16, no fp32 store: 6 bytes read, 2 written).
-  const int64_t cap = (int64_t)cus() * 4;
-  const bool nt = emit && !store && !overwrite;
+  // Launch policy, measured on MI355X for the three call kinds (blocks of
+  // 256 threads per CU, cache policy).
+  const int64_t cap = (int64_t)cus() * kAccBlocksPerCu;
   const bool vec = a16(grad) && (!acc || a16(acc)) && (!emit || a16(bf16_out));
   const int64_t work = vec ? std::max<int64_t>(n >> 3, 8) : n;
   const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256, cap));
-  if (vec && nt)
-    hipLaunchKernelGGL(accum_vec_kernel<true>, dim3(blocks), dim3(256), 0, stream, acc, grad, n,
-                       scale, flags, bf16_out);
-  else if (vec)
-    hipLaunchKernelGGL(accum_vec_kernel<false>, dim3(blocks), dim3(256), 0, stream, acc, grad, n,
-                       scale, flags, bf16_out);
+  if (vec)
+    hipLaunchKernelGGL(accum_vec_kernel<kAccPolicy>, dim3(blocks), dim3(256), 0, stream, acc,
+                       grad, n, scale, flags, bf16_out);
   else
     hipLaunchKernelGGL(accum_scalar_kernel, dim3(blocks), dim3(256), 0, stream, acc, grad, n,
                        scale, flags, bf16_out);

@@ -16,10 +16,11 @@
 //
 // Design (gfx950): the step is a pure HBM stream (2*N_d + 26 bytes per shard
 // element for bf16 contributions) with no reuse, so it is written as a
-// grid-stride loop in which each lane moves 8 elements per iteration with
-// 128-bit loads and stores (one 16-byte load per rank, two per fp32 state
-// array); the cache hint (non-temporal or not) and the blocks per CU follow
-// the measured read/write mix.  No LDS, no atomics, no MFMA: every output
+// grid-stride loop over chunks of 512 elements per wave, each lane moving
+// two 4-element pieces per chunk, laid out so that every load and store
+// instruction of a wave covers whole cache lines (8-byte bf16 and 16-byte
+// fp32 accesses); the cache hint (non-temporal or not) per stream and the
+// blocks per CU follow measurements.  No LDS, no atomics, no MFMA: every output
 // element belongs to exactly one lane, which makes the result independent of
 // the launch shape.  Each rank count that matters gets its own unrolled
 // instantiation; for large N_d the rank loads are issued in groups so that
@@ -105,7 +106,8 @@ __device__ __forceinline__ void adamw(float g, float& th, float& m, float& v, co
   v = v1;
 }
 
-// 8 consecutive contributions of one rank, as loaded (not yet widened).
+// 8 contributions of one rank, two pieces of 4 consecutive elements (a:
+// elements 0-3, b: elements 4-7), as loaded (not yet widened).
 template <int GT>
 struct Raw8 {
   f32x4 lo, hi;  // fused: the accumulator
@@ -124,19 +126,22 @@ struct Raw8<GT_F32> {
 // the master / m / v loads, and every store.
 enum : int { NT_CONTRIB = 1, NT_STATE = 2, NT_STORE = 4 };
 
+// Pieces at contribution indices ga and gb (multiples of 4).
 template <int GT, int NT, class Args>
-__device__ __forceinline__ Raw8<GT> load8(const Args& A, int q, int64_t gi) {
+__device__ __forceinline__ Raw8<GT> load8(const Args& A, int q, int64_t ga, int64_t gb) {
   constexpr bool nt = (NT & NT_CONTRIB) != 0;
   Raw8<GT> r;
-  if constexpr (GT == GT_BF16) {
-    r.w = ld_stream<nt>((const u32x4*)((const uint16_t*)A.g[q] + gi));
-  } else if constexpr (GT == GT_F32) {
-    r.lo = ld_stream<nt>((const f32x4*)((const float*)A.g[q] + gi));
-    r.hi = ld_stream<nt>((const f32x4*)((const float*)A.g[q] + gi + 4));
+  if constexpr (GT == GT_F32) {
+    r.lo = ld_stream<nt>((const f32x4*)((const float*)A.g[q] + ga));
+    r.hi = ld_stream<nt>((const f32x4*)((const float*)A.g[q] + gb));
   } else {
-    r.lo = ld_stream<nt>((const f32x4*)(A.a[q] + gi));
-    r.hi = ld_stream<nt>((const f32x4*)(A.a[q] + gi + 4));
-    r.w = ld_stream<nt>((const u32x4*)((const uint16_t*)A.g[q] + gi));
+    if constexpr (fused(GT)) {
+      r.lo = ld_stream<nt>((const f32x4*)(A.a[q] + ga));
+      r.hi = ld_stream<nt>((const f32x4*)(A.a[q] + gb));
+    }
+    const u32x2 a = ld_stream<nt>((const u32x2*)((const uint16_t*)A.g[q] + ga));
+    const u32x2 b = ld_stream<nt>((const u32x2*)((const uint16_t*)A.g[q] + gb));
+    r.w = u32x4{a.x, a.y, b.x, b.y};
   }
   return r;
 }
@@ -189,20 +194,21 @@ __device__ __forceinline__ float load_one(const Args& A, int q, int64_t gi) {
     return fold<GT>(A.a[q][gi], bf16_one(((const uint16_t*)A.g[q])[gi]), A.acc_scale);
 }
 
-// Sum of the N_d contributions of 8 consecutive elements, ascending rank.
-// The loads of up to GROUP ranks are issued before their adds.
+// Sum of the N_d contributions of the 8 elements of two pieces, ascending
+// rank.  The loads of up to GROUP ranks are issued before their adds.
 // The fused contributions at large N_d keep the group loop rolled: fully
 // unrolled, the scheduler hoists loads of later groups and spills.
 template <int ND, int GROUP, int NT, int GT>
-__device__ __forceinline__ void reduce8(float acc[8], const ArgsFor<ND, GT>& A, int64_t gi) {
-  widen8<GT>(acc, load8<GT, NT>(A, 0, gi), A);
+__device__ __forceinline__ void reduce8(float acc[8], const ArgsFor<ND, GT>& A, int64_t ga,
+                                        int64_t gb) {
+  widen8<GT>(acc, load8<GT, NT>(A, 0, ga, gb), A);
   if constexpr (fused(GT) && ND > 16) {
 #pragma unroll 1
     for (int q0 = 1; q0 < ND; q0 += GROUP) {
       Raw8<GT> w[GROUP];
 #pragma unroll
       for (int u = 0; u < GROUP; ++u)
-        if (q0 + u < ND) w[u] = load8<GT, NT>(A, q0 + u, gi);
+        if (q0 + u < ND) w[u] = load8<GT, NT>(A, q0 + u, ga, gb);
 #pragma unroll
       for (int u = 0; u < GROUP; ++u)
         if (q0 + u < ND) add8<GT>(acc, w[u], A);
@@ -214,7 +220,7 @@ __device__ __forceinline__ void reduce8(float acc[8], const ArgsFor<ND, GT>& A, 
     Raw8<GT> w[GROUP];
 #pragma unroll
     for (int u = 0; u < GROUP; ++u)
-      if (q0 + u < ND) w[u] = load8<GT, NT>(A, q0 + u, gi);
+      if (q0 + u < ND) w[u] = load8<GT, NT>(A, q0 + u, ga, gb);
 #pragma unroll
     for (int u = 0; u < GROUP; ++u)
       if (q0 + u < ND) add8<GT>(acc, w[u], A);
@@ -223,9 +229,10 @@ __device__ __forceinline__ void reduce8(float acc[8], const ArgsFor<ND, GT>& A, 
 
 // Runtime rank count.
 template <int NT, int GT>
-__device__ __forceinline__ void reduce8_dyn(float acc[8], const ArgsFor<0, GT>& A, int64_t gi) {
-  widen8<GT>(acc, load8<GT, NT>(A, 0, gi), A);
-  for (int q = 1; q < A.nd; ++q) add8<GT>(acc, load8<GT, NT>(A, q, gi), A);
+__device__ __forceinline__ void reduce8_dyn(float acc[8], const ArgsFor<0, GT>& A, int64_t ga,
+                                            int64_t gb) {
+  widen8<GT>(acc, load8<GT, NT>(A, 0, ga, gb), A);
+  for (int q = 1; q < A.nd; ++q) add8<GT>(acc, load8<GT, NT>(A, q, ga, gb), A);
 }
 
 __device__ __forceinline__ int64_t flat_of(const Region& r, int64_t e) {
@@ -257,24 +264,25 @@ __device__ __forceinline__ void step_one(const Args& A, int64_t e, bool map) {
   step_at<GT>(A, i, (map && A.flat_grad) ? f : i, (map && A.slot_out) ? f : i);
 }
 
-// 8 consecutive elements with 128-bit accesses: shard index i, contribution
-// index gi, output index oi (all multiples of 8 on 16-byte aligned bases).
+// Two pieces of 4 consecutive elements: piece a at shard index ia,
+// contribution index ga, output index oa; piece b likewise (all multiples of
+// 4 on 16-byte aligned bases: 16-byte fp32 and 8-byte bf16 accesses).
 template <int ND, int GROUP, int NT, int GT>
-__device__ __forceinline__ void step8(const ArgsFor<ND, GT>& A, int64_t i, int64_t gi,
-                                      int64_t oi) {
+__device__ __forceinline__ void step8(const ArgsFor<ND, GT>& A, int64_t ia, int64_t ga,
+                                      int64_t oa, int64_t ib, int64_t gb, int64_t ob) {
   float acc[8];
   if constexpr (ND > 0)
-    reduce8<ND, GROUP, NT, GT>(acc, A, gi);
+    reduce8<ND, GROUP, NT, GT>(acc, A, ga, gb);
   else
-    reduce8_dyn<NT, GT>(acc, A, gi);
+    reduce8_dyn<NT, GT>(acc, A, ga, gb);
 
   constexpr bool nts = (NT & NT_STATE) != 0, ntw = (NT & NT_STORE) != 0;
-  const f32x4 th0 = ld_stream<nts>((const f32x4*)(A.master + i));
-  const f32x4 th1 = ld_stream<nts>((const f32x4*)(A.master + i + 4));
-  const f32x4 m0 = ld_stream<nts>((const f32x4*)(A.m + i));
-  const f32x4 m1 = ld_stream<nts>((const f32x4*)(A.m + i + 4));
-  const f32x4 v0 = ld_stream<nts>((const f32x4*)(A.v + i));
-  const f32x4 v1 = ld_stream<nts>((const f32x4*)(A.v + i + 4));
+  const f32x4 th0 = ld_stream<nts>((const f32x4*)(A.master + ia));
+  const f32x4 th1 = ld_stream<nts>((const f32x4*)(A.master + ib));
+  const f32x4 m0 = ld_stream<nts>((const f32x4*)(A.m + ia));
+  const f32x4 m1 = ld_stream<nts>((const f32x4*)(A.m + ib));
+  const f32x4 v0 = ld_stream<nts>((const f32x4*)(A.v + ia));
+  const f32x4 v1 = ld_stream<nts>((const f32x4*)(A.v + ib));
   float th[8] = {th0.x, th0.y, th0.z, th0.w, th1.x, th1.y, th1.z, th1.w};
   float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
   float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -284,60 +292,70 @@ __device__ __forceinline__ void step8(const ArgsFor<ND, GT>& A, int64_t i, int64
     g[k] = average<((ND & (ND - 1)) == 0 ? ND : 0)>(acc[k], A);
     adamw(g[k], th[k], mm[k], vv[k], A.k);
   }
-  st_stream<ntw>((f32x4*)(A.master + i), f32x4{th[0], th[1], th[2], th[3]});
-  st_stream<ntw>((f32x4*)(A.master + i + 4), f32x4{th[4], th[5], th[6], th[7]});
-  st_stream<ntw>((f32x4*)(A.m + i), f32x4{mm[0], mm[1], mm[2], mm[3]});
-  st_stream<ntw>((f32x4*)(A.m + i + 4), f32x4{mm[4], mm[5], mm[6], mm[7]});
-  st_stream<ntw>((f32x4*)(A.v + i), f32x4{vv[0], vv[1], vv[2], vv[3]});
-  st_stream<ntw>((f32x4*)(A.v + i + 4), f32x4{vv[4], vv[5], vv[6], vv[7]});
-  st_stream<ntw>((u32x4*)(A.pout + oi),
-                u32x4{bf16_pack2(th[0], th[1]), bf16_pack2(th[2], th[3]),
-                      bf16_pack2(th[4], th[5]), bf16_pack2(th[6], th[7])});
+  st_stream<ntw>((f32x4*)(A.master + ia), f32x4{th[0], th[1], th[2], th[3]});
+  st_stream<ntw>((f32x4*)(A.master + ib), f32x4{th[4], th[5], th[6], th[7]});
+  st_stream<ntw>((f32x4*)(A.m + ia), f32x4{mm[0], mm[1], mm[2], mm[3]});
+  st_stream<ntw>((f32x4*)(A.m + ib), f32x4{mm[4], mm[5], mm[6], mm[7]});
+  st_stream<ntw>((f32x4*)(A.v + ia), f32x4{vv[0], vv[1], vv[2], vv[3]});
+  st_stream<ntw>((f32x4*)(A.v + ib), f32x4{vv[4], vv[5], vv[6], vv[7]});
+  st_stream<ntw>((u32x2*)(A.pout + oa), u32x2{bf16_pack2(th[0], th[1]), bf16_pack2(th[2], th[3])});
+  st_stream<ntw>((u32x2*)(A.pout + ob), u32x2{bf16_pack2(th[4], th[5]), bf16_pack2(th[6], th[7])});
   if (A.gout) {
-    st_stream<ntw>((f32x4*)(A.gout + i), f32x4{g[0], g[1], g[2], g[3]});
-    st_stream<ntw>((f32x4*)(A.gout + i + 4), f32x4{g[4], g[5], g[6], g[7]});
+    st_stream<ntw>((f32x4*)(A.gout + ia), f32x4{g[0], g[1], g[2], g[3]});
+    st_stream<ntw>((f32x4*)(A.gout + ib), f32x4{g[4], g[5], g[6], g[7]});
   }
 }
 
-// Vector path over one Region: 8 elements per lane per iteration,
-// grid-stride.  Requires 16-byte aligned bases and i0 % 8 == 0; when mapping,
-// flat0 % 8 == 0 and (part 0 is one bucket, or seg % 8 == 0 and
-// pstride % 8 == 0), and if part 1 exists n0 % 8 == 0 and flat1 % 8 == 0, so
-// that no vector straddles a bucket and every vector address is aligned.
+// Moves a piece's bucket coordinates (b, j) forward by adv elements.
+__device__ __forceinline__ void advance(int64_t& b, int64_t& j, int64_t adv, int64_t seg) {
+  j += adv;
+  if (j >= seg) {
+    const int64_t q = j / seg;
+    b += q;
+    j -= q * seg;
+  }
+}
+
+// Vector path over one Region, grid-stride over chunks of 512 elements: in
+// each chunk, lane l of a wave takes the 4-element pieces at 4l and 256 + 4l,
+// so that every load and store instruction of the wave covers one
+// contiguous span (1 KB of fp32, 512 bytes of bf16) and each cache line is
+// fetched by one instruction.  Requires 16-byte aligned bases and
+// i0 % 4 == 0; when mapping, flat0 % 4 == 0 and (part 0 is one bucket, or
+// seg % 4 == 0 and pstride % 4 == 0), and if part 1 exists n0 % 4 == 0 and
+// flat1 % 4 == 0, so that no piece straddles a bucket and every piece
+// address is aligned.  The elements after the last full chunk run one per
+// thread.
 template <int ND, bool MAP, int GROUP, int NT, int GT>
 __global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND, GT> A) {
-  const int64_t n = A.reg.n;
-  const int64_t nv0 = A.reg.n0 >> 3;
-  const int64_t nvec = (A.reg.n0 == n) ? nv0 : nv0 + ((n - A.reg.n0) >> 3);
+  const Region& R = A.reg;
+  const int64_t n = R.n;
+  const int64_t nchunk = n >> 9;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t T = (int64_t)gridDim.x * blockDim.x;
-  const int64_t adv = T << 3;
-  int64_t b = 0, j = 0;
+  const int64_t wave = tid >> 6, W = T >> 6, adv = W << 9;
+  int64_t ea = (wave << 9) + ((threadIdx.x & 63) << 2);
+  int64_t ba = 0, ja = 0, bb = 0, jb = 0;
   if (MAP) {
-    b = (tid << 3) / A.reg.seg;
-    j = (tid << 3) - b * A.reg.seg;
+    ba = ea / R.seg;
+    ja = ea - ba * R.seg;
+    bb = (ea + 256) / R.seg;
+    jb = ea + 256 - bb * R.seg;
   }
-  for (int64_t vi = tid; vi < nvec; vi += T) {
-    const int64_t i = A.reg.i0 + (vi << 3);
-    int64_t f = i;
+  for (int64_t c = wave; c < nchunk; c += W, ea += adv) {
+    const int64_t eb = ea + 256;
+    const int64_t ia = R.i0 + ea, ib = R.i0 + eb;
+    int64_t fa = ia, fb = ib;
     if (MAP) {
-      if (vi < nv0) {
-        f = A.reg.flat0 + b * A.reg.pstride + j;
-        j += adv;
-        if (j >= A.reg.seg) {
-          const int64_t q = j / A.reg.seg;
-          b += q;
-          j -= q * A.reg.seg;
-        }
-      } else {
-        f = A.reg.flat1 + ((vi - nv0) << 3);
-      }
+      fa = ea < R.n0 ? R.flat0 + ba * R.pstride + ja : R.flat1 + (ea - R.n0);
+      fb = eb < R.n0 ? R.flat0 + bb * R.pstride + jb : R.flat1 + (eb - R.n0);
+      advance(ba, ja, adv, R.seg);
+      advance(bb, jb, adv, R.seg);
     }
-    step8<ND, GROUP, NT, GT>(A, i, (MAP && A.flat_grad) ? f : i, (MAP && A.slot_out) ? f : i);
+    const bool fg = MAP && A.flat_grad, so = MAP && A.slot_out;
+    step8<ND, GROUP, NT, GT>(A, ia, fg ? fa : ia, so ? fa : ia, ib, fg ? fb : ib, so ? fb : ib);
   }
-  // the elements after the last full vector, one per lane
-  const int64_t tail0 = (nvec == nv0) ? (nv0 << 3) : A.reg.n0 + ((nvec - nv0) << 3);
-  if (tid < n - tail0) step_one<GT>(A, tail0 + tid, MAP);
+  for (int64_t e = (nchunk << 9) + tid; e < n; e += T) step_one<GT>(A, e, MAP);
 }
 
 // Many single-bucket regions in one launch (the per-parameter layout, where
@@ -347,9 +365,10 @@ __global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND, GT> A) 
 // its length).  The work is cut into tiles of blockDim.x*8 elements; blocks
 // take tiles grid-stride and find a tile's region by binary search over the
 // tile prefix sums, so a 38.6M-element embedding and 96-element norm slices
-// share one launch without idle blocks.  Regions whose shard or flat start
-// is not a multiple of 8 (or every region, when a base pointer is not
-// 16-byte aligned) run element by element.  20 bytes per region: a launch
+// share one launch without idle blocks.  Within a tile, each wave takes 512
+// elements in the chunk mapping of step_vec_kernel.  Regions whose shard or
+// flat start is not a multiple of 4 (or every region, when a base pointer is
+// not 16-byte aligned) run element by element.  20 bytes per region: a launch
 // takes as many regions as fit next to the kernel's other arguments in
 // 4 KB (191 for bf16 contributions at N_d = 8).
 template <int CAP>
@@ -388,15 +407,21 @@ __global__ void __launch_bounds__(256) step_table_kernel(const ArgsFor<ND, GT> A
     }
     const int64_t r0 = T.i_base + T.e0[lo], f0 = T.f0[lo];
     const int64_t n = T.e0[lo + 1] - T.e0[lo];
-    const int64_t e0 = (int64_t)(tile - T.tile0[lo]) * span + ((int64_t)threadIdx.x << 3);
-    if (e0 >= n) continue;
-    const int64_t i = r0 + e0, f = f0 + e0;
-    const int64_t gi = A.flat_grad ? f : i, oi = A.slot_out ? f : i;
-    if (T.vec_ok && ((r0 | f0) & 7) == 0 && e0 + 8 <= n) {
-      step8<ND, GROUP, NT, GT>(A, i, gi, oi);
+    // the pieces of this lane in the tile: each wave takes 512 elements
+    const int64_t ea = (int64_t)(tile - T.tile0[lo]) * span + ((threadIdx.x >> 6) << 9) +
+                       ((threadIdx.x & 63) << 2);
+    const int64_t eb = ea + 256;
+    if (ea >= n) continue;
+    const int64_t ia = r0 + ea, fa = f0 + ea, ib = r0 + eb, fb = f0 + eb;
+    const int64_t ga = A.flat_grad ? fa : ia, oa = A.slot_out ? fa : ia;
+    const int64_t gb = A.flat_grad ? fb : ib, ob = A.slot_out ? fb : ib;
+    if (T.vec_ok && ((r0 | f0) & 3) == 0 && eb + 4 <= n) {
+      step8<ND, GROUP, NT, GT>(A, ia, ga, oa, ib, gb, ob);
     } else {
-      const int64_t m = n - e0 < 8 ? n - e0 : 8;
-      for (int64_t e = 0; e < m; ++e) step_at<GT>(A, i + e, gi + e, oi + e);
+      const int64_t ma = n - ea < 4 ? n - ea : 4;
+      for (int64_t e = 0; e < ma; ++e) step_at<GT>(A, ia + e, ga + e, oa + e);
+      const int64_t mb = n - eb < 4 ? n - eb : 4;
+      for (int64_t e = 0; e < mb; ++e) step_at<GT>(A, ib + e, gb + e, ob + e);
     }
   }
 }
@@ -470,24 +495,23 @@ int cu_count() {
 //   accumulator + last micro-batch: ordinary accesses, one 256-thread block
 //     per CU (12.6 ms against 13.2 with two).
 constexpr bool read_dominated(int nd, int gt) { return nd * contrib_bytes(gt) >= 64; }
-// Measured on the tuned llama8b / llama70b buffers (mix kernel and step):
-// bf16 contributions, one 16-byte load per lane and 8 elements, stream
-// best non-temporal (+2 % at N_d = 8 and 64, +8 % at 15.6M elements), and
-// non-temporal stores add a little.  Loads that fetch a cache line in two
-// halves (fp32 contributions, accumulators, the fp32 state: two 16-byte
-// loads per lane) lose 5-10 % when non-temporal, so they stay ordinary.
-constexpr int cache_policy(int gt) { return gt == GT_BF16 ? NT_CONTRIB | NT_STORE : 0; }
+// Cache policy, measured on the tuned llama8b / llama70b buffers (every
+// policy and launch shape, N_d = 8 to 64): with each cache line fetched by a
+// single instruction (the chunk mapping of step_vec_kernel), non-temporal
+// loads and stores of every stream are best for bf16 contributions (2-3 %
+// over ordinary state loads) and whenever the contributions dominate the
+// bytes; for fp32 or accumulator contributions at small N_d, non-temporal
+// contribution loads with ordinary state accesses.
+constexpr int cache_policy(int nd, int gt) {
+  return (gt == GT_BF16 || read_dominated(nd, gt)) ? NT_CONTRIB | NT_STATE | NT_STORE
+                                                   : NT_CONTRIB;
+}
 struct Policy {
   int blocks_per_cu, threads;
 };
 Policy default_policy(int nd, int gt) {
-  if (read_dominated(nd, gt)) return Policy{1, 256};
-  switch (gt) {
-    case GT_F32: return Policy{2, 256};
-    case GT_ACC_BF16:
-    case GT_ACC_F32: return Policy{1, 256};
-    default: return Policy{2, 128};
-  }
+  if (gt == GT_F32 && !read_dominated(nd, gt)) return Policy{2, 128};
+  return Policy{1, 256};
 }
 
 // What one launch covers: a Region (affine addressing, with or without the
@@ -554,7 +578,12 @@ int launch_nt(const Call& c, const Work& w, hipStream_t s) {
 
 template <int ND, int GT, int KIND>
 int launch(const Call& c, const Work& w, hipStream_t s) {
-  return launch_nt<ND, GT, KIND, cache_policy(GT)>(c, w, s);
+  if constexpr (ND > 0)
+    return launch_nt<ND, GT, KIND, cache_policy(ND, GT)>(c, w, s);
+  else
+    return read_dominated(c.nd, GT)
+               ? launch_nt<0, GT, KIND, cache_policy(ZERO_MAX_ND, GT)>(c, w, s)
+               : launch_nt<0, GT, KIND, cache_policy(1, GT)>(c, w, s);
 }
 
 template <int GT, int KIND>
@@ -697,13 +726,17 @@ int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int3
     for (int64_t b = b0; b < b1; ++b)
       if ((L->bucket_slice(b) + span_e - 1) / span_e >= kMaxTableTiles) return ZERO_ERANGE;
     const int tcap = table_cap(nd, c.gt);
+    // table launches fill the chip better with two blocks per CU: each
+    // block does one chunk per wave between region look-ups (GPT-2, 148
+    // tensors: 0.137 ms with one block per CU, 0.123 ms with two)
+    const int tblocks = ls.blocks_cap > 0 ? ls.blocks_cap : cu_count() * 2;
     HostTable T;
     T.count = 0;
     T.vec_ok = allow_vec ? 1 : 0;
     auto flush = [&]() -> int {
       if (T.count == 0) return ZERO_OK;
       const int64_t total = T.tile0[T.count];
-      const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(total, cap));
+      const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(total, tblocks));
       const Work w{nullptr, &T, blocks, threads};
       const int rc = dispatch<K_TABLE>(c, w, stream);
       T.count = 0;
@@ -749,14 +782,14 @@ int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int3
   const int64_t n_all = i_end - i_begin;
   if (!map) {
     regs.push_back(Region{i_begin, n_all, n_all, n_all, 0, 0, 0});
-    vec.push_back(allow_vec && i_begin % 8 == 0);
+    vec.push_back(allow_vec && i_begin % 4 == 0);
   } else if (L->nb == 1 || L->s_last == L->s_full) {
     // every bucket has the same slice: one affine part
     const bool one = b1 - b0 == 1;
     const int64_t flat0 = b0 * L->p_full + r * L->s_full;
     regs.push_back(Region{i_begin, n_all, n_all, L->s_full, L->p_full, flat0, 0});
-    vec.push_back(allow_vec && i_begin % 8 == 0 && flat0 % 8 == 0 &&
-                  (one || (L->s_full % 8 == 0 && L->p_full % 8 == 0)));
+    vec.push_back(allow_vec && i_begin % 4 == 0 && flat0 % 4 == 0 &&
+                  (one || (L->s_full % 4 == 0 && L->p_full % 4 == 0)));
   } else {
     const bool has_last = b1 == L->nb;
     const int64_t nf = (has_last ? L->nb - 1 : b1) - b0;  // full buckets in the range
@@ -766,10 +799,10 @@ int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int3
     if (nf == 0) {
       // the last bucket alone
       regs.push_back(Region{i_begin, L->s_last, L->s_last, L->s_last, L->p_last, flat1, 0});
-      vec.push_back(allow_vec && i_begin % 8 == 0 && flat1 % 8 == 0);
+      vec.push_back(allow_vec && i_begin % 4 == 0 && flat1 % 4 == 0);
     } else {
-      const bool v0 = allow_vec && L->s_full % 8 == 0 && L->p_full % 8 == 0;
-      const bool v1 = !has_last || (allow_vec && flat1 % 8 == 0);
+      const bool v0 = allow_vec && L->s_full % 4 == 0 && L->p_full % 4 == 0;
+      const bool v1 = !has_last || (allow_vec && flat1 % 4 == 0);
       if (v0 && v1) {
         regs.push_back(Region{i_begin, n0, n_all, L->s_full, L->p_full, flat0, flat1});
         vec.push_back(true);

@@ -40,7 +40,7 @@
  *     no fused multiply-add, subnormals kept, correctly rounded division
  *     and square root.  Results do not depend on the launch configuration.
  *   - Any pointer alignment is accepted; 16-byte aligned buffers take the
- *     128-bit vector path, others a scalar path with the same results.
+ *     vector path, others a scalar path with the same results.
  *   - Entry points may be called from several host threads at once (no
  *     mutable global state apart from a per-device count of compute units);
  *     calls that write the same buffers must be ordered by the caller.

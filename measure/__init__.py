@@ -37,7 +37,7 @@ def stream_ceiling(grads, state, out, n: int, reps: int = 5):
     nd = len(grads)
     g = (C.c_void_p * nd)(*[t.data_ptr() for t in grads])
     s = (C.c_void_p * 3)(*[t.data_ptr() for t in state])
-    n = n // 8 * 8
+    n = n // 512 * 512
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     stream = torch.cuda.current_stream()
     best = (0.0, None)
@@ -70,7 +70,7 @@ def stream_probes(grads, state, out, n: int, reps: int = 5):
     nd = len(grads)
     g = (C.c_void_p * nd)(*[t.data_ptr() for t in grads])
     s = (C.c_void_p * 3)(*[t.data_ptr() for t in state])
-    n = n // 8 * 8
+    n = n // 512 * 512
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     stream = torch.cuda.current_stream()
     res = {}
