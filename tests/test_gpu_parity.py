@@ -228,6 +228,9 @@ EDGE = [
     ([4096 * 7 + 5], 4096, 7, 6, "flat", "shard"),
     ([70000, 3], 16384, 8, 7, "flat", "ag_slot"),           # ragged last bucket (slice % 8 != 0)
     ([50000], 8008, 8, 3, "flat", "ag_slot"),               # slice 1001: unaligned flat slots
+    ([50000], 8032, 8, 3, "flat", "ag_slot"),               # slice 1004: 4- but not 8-aligned
+    ([4 * 2503], 0, 4, 1, "compact", "shard"),              # 2503: 4 full chunks + 455 tail
+    ([20 * 1040 + 12], 1040, 4, 2, "flat", "ag_slot"),      # slice 260: chunks cross buckets
     ([20000, 20001], 0, 16, 15, "compact", "ag_slot"),
     ([65536 + 13], 0, 32, 31, "flat", "ag_slot"),
     ([64 * 300 + 1], 6400, 64, 63, "compact", "shard"),     # N_d = 64 with padded tails
