@@ -1,7 +1,8 @@
 """The C ABI from plain C programs compiled with gcc as C11 against
-include/zero_shard.h and linked to the built library: tests/abi_c_smoke.c
-(host-side entry points, CPU) and tests/abi_c_step.c (three shard steps on
-the GPU with hipMalloc'd memory, compared with the CPU oracle)."""
+include/zero_shard.h and linked to the built library (tests/build_c_clients.py,
+run by __graft_entry__.build()): tests/abi_c_smoke.c (host-side entry points,
+CPU) and tests/abi_c_step.c (three shard steps on the GPU with hipMalloc'd
+memory, compared with the CPU oracle)."""
 import os
 import subprocess
 
@@ -13,15 +14,17 @@ import fsdp_sharded_optimizer_step_amd as z
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def test_plain_c_client(tmp_path):
-    lib_dir = os.path.dirname(z.binding.LIB_PATH)
+def _client(name):
+    """The prebuilt client (built by __graft_entry__.build())."""
+    import build_c_clients
+    exe = build_c_clients.exe_path(name)
+    assert os.path.exists(exe), f"{exe} is not built; run __graft_entry__.build()"
+    return exe
+
+
+def test_plain_c_client():
     assert os.path.exists(z.binding.LIB_PATH), "library not built"
-    exe = str(tmp_path / "abi_c_smoke")
-    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
-                    "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
-                    os.path.join(ROOT, "tests", "abi_c_smoke.c"), "-L", lib_dir, "-lzero_shard",
-                    f"-Wl,-rpath,{lib_dir}", "-o", exe], check=True)
-    out = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    out = subprocess.run([_client("abi_c_smoke")], capture_output=True, text=True, timeout=60)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "ok"
 
@@ -29,13 +32,7 @@ def test_plain_c_client(tmp_path):
 @pytest.mark.gpu
 def test_plain_c_client_runs_the_step_on_the_gpu(tmp_path):
     import oracle
-    lib_dir = os.path.dirname(z.binding.LIB_PATH)
-    exe = str(tmp_path / "abi_c_step")
-    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
-                    "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
-                    os.path.join(ROOT, "tests", "abi_c_step.c"), "-L", lib_dir, "-lzero_shard",
-                    "-L", "/opt/rocm/lib", "-lamdhip64", f"-Wl,-rpath,{lib_dir}",
-                    "-Wl,-rpath,/opt/rocm/lib", "-o", exe], check=True)
+    exe = _client("abi_c_step")
     path = str(tmp_path / "out.bin")
     out = subprocess.run([exe, path], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stderr
