@@ -51,11 +51,14 @@ def step_kernel_name(n_d: int, mapped: bool) -> str:
     """The step_vec_kernel instantiation the library launches for bf16
     contributions (its name in rocprofv3 traces): <N_d or 0 for the runtime
     loop, flat addressing, ranks loaded per group, cache policy (7: every
-    load and store non-temporal), dtype 0>."""
+    load and store non-temporal), dtype 0, pairs of 4-element pieces per
+    lane (2 from N_d = 64 on, with 8 ranks per group)>."""
     nd = n_d if n_d in (2, 4, 8, 16, 32, 64) else 0
-    group = min(16, nd - 1) if nd > 1 else 1
+    pairs = 2 if nd >= 64 else 1
+    gmax = 8 if pairs > 1 else 16
+    group = min(gmax, nd - 1) if nd > 1 else 1
     b = lambda x: "true" if x else "false"
-    return f"step_vec_kernel<{nd}, {b(mapped)}, {group}, 7, 0>"
+    return f"step_vec_kernel<{nd}, {b(mapped)}, {group}, 7, 0, {pairs}>"
 
 
 def traffic_from_profiles(workload: str, n_launch_bytes: float):

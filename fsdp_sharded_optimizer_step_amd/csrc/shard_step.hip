@@ -194,45 +194,61 @@ __device__ __forceinline__ float load_one(const Args& A, int q, int64_t gi) {
     return fold<GT>(A.a[q][gi], bf16_one(((const uint16_t*)A.g[q])[gi]), A.acc_scale);
 }
 
-// Sum of the N_d contributions of the 8 elements of two pieces, ascending
-// rank.  The loads of up to GROUP ranks are issued before their adds.
-// The fused contributions at large N_d keep the group loop rolled: fully
-// unrolled, the scheduler hoists loads of later groups and spills.
-template <int ND, int GROUP, int NT, int GT>
-__device__ __forceinline__ void reduce8(float acc[8], const ArgsFor<ND, GT>& A, int64_t ga,
-                                        int64_t gb) {
-  widen8<GT>(acc, load8<GT, NT>(A, 0, ga, gb), A);
+// Sum of the N_d contributions of NPAIR pairs of pieces (8 elements per
+// pair), ascending rank.  The loads of up to GROUP ranks (every pair) are
+// issued before their adds.  The fused contributions at large N_d keep the
+// group loop rolled: fully unrolled, the scheduler hoists loads of later
+// groups and spills.
+template <int ND, int GROUP, int NT, int GT, int NPAIR>
+__device__ __forceinline__ void reduce_pairs(float (&acc)[NPAIR][8], const ArgsFor<ND, GT>& A,
+                                             const int64_t (&gp)[2 * NPAIR]) {
+#pragma unroll
+  for (int h = 0; h < NPAIR; ++h)
+    widen8<GT>(acc[h], load8<GT, NT>(A, 0, gp[2 * h], gp[2 * h + 1]), A);
   if constexpr (fused(GT) && ND > 16) {
 #pragma unroll 1
     for (int q0 = 1; q0 < ND; q0 += GROUP) {
-      Raw8<GT> w[GROUP];
+      Raw8<GT> w[GROUP][NPAIR];
 #pragma unroll
       for (int u = 0; u < GROUP; ++u)
-        if (q0 + u < ND) w[u] = load8<GT, NT>(A, q0 + u, ga, gb);
+        if (q0 + u < ND)
+#pragma unroll
+          for (int h = 0; h < NPAIR; ++h) w[u][h] = load8<GT, NT>(A, q0 + u, gp[2 * h], gp[2 * h + 1]);
 #pragma unroll
       for (int u = 0; u < GROUP; ++u)
-        if (q0 + u < ND) add8<GT>(acc, w[u], A);
+        if (q0 + u < ND)
+#pragma unroll
+          for (int h = 0; h < NPAIR; ++h) add8<GT>(acc[h], w[u][h], A);
     }
     return;
   }
 #pragma unroll
   for (int q0 = 1; q0 < ND; q0 += GROUP) {
-    Raw8<GT> w[GROUP];
+    Raw8<GT> w[GROUP][NPAIR];
 #pragma unroll
     for (int u = 0; u < GROUP; ++u)
-      if (q0 + u < ND) w[u] = load8<GT, NT>(A, q0 + u, ga, gb);
+      if (q0 + u < ND)
+#pragma unroll
+        for (int h = 0; h < NPAIR; ++h) w[u][h] = load8<GT, NT>(A, q0 + u, gp[2 * h], gp[2 * h + 1]);
 #pragma unroll
     for (int u = 0; u < GROUP; ++u)
-      if (q0 + u < ND) add8<GT>(acc, w[u], A);
+      if (q0 + u < ND)
+#pragma unroll
+        for (int h = 0; h < NPAIR; ++h) add8<GT>(acc[h], w[u][h], A);
   }
 }
 
 // Runtime rank count.
-template <int NT, int GT>
-__device__ __forceinline__ void reduce8_dyn(float acc[8], const ArgsFor<0, GT>& A, int64_t ga,
-                                            int64_t gb) {
-  widen8<GT>(acc, load8<GT, NT>(A, 0, ga, gb), A);
-  for (int q = 1; q < A.nd; ++q) add8<GT>(acc, load8<GT, NT>(A, q, ga, gb), A);
+template <int NT, int GT, int NPAIR>
+__device__ __forceinline__ void reduce_pairs_dyn(float (&acc)[NPAIR][8], const ArgsFor<0, GT>& A,
+                                                 const int64_t (&gp)[2 * NPAIR]) {
+#pragma unroll
+  for (int h = 0; h < NPAIR; ++h)
+    widen8<GT>(acc[h], load8<GT, NT>(A, 0, gp[2 * h], gp[2 * h + 1]), A);
+  for (int q = 1; q < A.nd; ++q)
+#pragma unroll
+    for (int h = 0; h < NPAIR; ++h)
+      add8<GT>(acc[h], load8<GT, NT>(A, q, gp[2 * h], gp[2 * h + 1]), A);
 }
 
 __device__ __forceinline__ int64_t flat_of(const Region& r, int64_t e) {
@@ -264,45 +280,57 @@ __device__ __forceinline__ void step_one(const Args& A, int64_t e, bool map) {
   step_at<GT>(A, i, (map && A.flat_grad) ? f : i, (map && A.slot_out) ? f : i);
 }
 
-// Two pieces of 4 consecutive elements: piece a at shard index ia,
-// contribution index ga, output index oa; piece b likewise (all multiples of
-// 4 on 16-byte aligned bases: 16-byte fp32 and 8-byte bf16 accesses).
-template <int ND, int GROUP, int NT, int GT>
-__device__ __forceinline__ void step8(const ArgsFor<ND, GT>& A, int64_t ia, int64_t ga,
-                                      int64_t oa, int64_t ib, int64_t gb, int64_t ob) {
-  float acc[8];
+// 2*NPAIR pieces of 4 consecutive elements: piece k at shard index ip[k],
+// contribution index gp[k], output index op[k] (all multiples of 4 on
+// 16-byte aligned bases: 16-byte fp32 and 8-byte bf16 accesses).  Every
+// load of the pieces is issued before the first store.
+template <int ND, int GROUP, int NT, int GT, int NPAIR>
+__device__ __forceinline__ void step_pieces(const ArgsFor<ND, GT>& A,
+                                            const int64_t (&ip)[2 * NPAIR],
+                                            const int64_t (&gp)[2 * NPAIR],
+                                            const int64_t (&op)[2 * NPAIR]) {
+  constexpr int NPC = 2 * NPAIR;
+  float acc[NPAIR][8];
   if constexpr (ND > 0)
-    reduce8<ND, GROUP, NT, GT>(acc, A, ga, gb);
+    reduce_pairs<ND, GROUP, NT, GT, NPAIR>(acc, A, gp);
   else
-    reduce8_dyn<NT, GT>(acc, A, ga, gb);
+    reduce_pairs_dyn<NT, GT, NPAIR>(acc, A, gp);
 
   constexpr bool nts = (NT & NT_STATE) != 0, ntw = (NT & NT_STORE) != 0;
-  const f32x4 th0 = ld_stream<nts>((const f32x4*)(A.master + ia));
-  const f32x4 th1 = ld_stream<nts>((const f32x4*)(A.master + ib));
-  const f32x4 m0 = ld_stream<nts>((const f32x4*)(A.m + ia));
-  const f32x4 m1 = ld_stream<nts>((const f32x4*)(A.m + ib));
-  const f32x4 v0 = ld_stream<nts>((const f32x4*)(A.v + ia));
-  const f32x4 v1 = ld_stream<nts>((const f32x4*)(A.v + ib));
-  float th[8] = {th0.x, th0.y, th0.z, th0.w, th1.x, th1.y, th1.z, th1.w};
-  float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-  float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-  float g[8];
+  f32x4 th[NPC], mm[NPC], vv[NPC];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    g[k] = average<((ND & (ND - 1)) == 0 ? ND : 0)>(acc[k], A);
-    adamw(g[k], th[k], mm[k], vv[k], A.k);
+  for (int k = 0; k < NPC; ++k) th[k] = ld_stream<nts>((const f32x4*)(A.master + ip[k]));
+#pragma unroll
+  for (int k = 0; k < NPC; ++k) mm[k] = ld_stream<nts>((const f32x4*)(A.m + ip[k]));
+#pragma unroll
+  for (int k = 0; k < NPC; ++k) vv[k] = ld_stream<nts>((const f32x4*)(A.v + ip[k]));
+  f32x4 g[NPC];
+#pragma unroll
+  for (int k = 0; k < NPC; ++k) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float gk = average<((ND & (ND - 1)) == 0 ? ND : 0)>(acc[k >> 1][4 * (k & 1) + e], A);
+      float t = th[k][e], m = mm[k][e], v = vv[k][e];
+      adamw(gk, t, m, v, A.k);
+      th[k][e] = t;
+      mm[k][e] = m;
+      vv[k][e] = v;
+      g[k][e] = gk;
+    }
   }
-  st_stream<ntw>((f32x4*)(A.master + ia), f32x4{th[0], th[1], th[2], th[3]});
-  st_stream<ntw>((f32x4*)(A.master + ib), f32x4{th[4], th[5], th[6], th[7]});
-  st_stream<ntw>((f32x4*)(A.m + ia), f32x4{mm[0], mm[1], mm[2], mm[3]});
-  st_stream<ntw>((f32x4*)(A.m + ib), f32x4{mm[4], mm[5], mm[6], mm[7]});
-  st_stream<ntw>((f32x4*)(A.v + ia), f32x4{vv[0], vv[1], vv[2], vv[3]});
-  st_stream<ntw>((f32x4*)(A.v + ib), f32x4{vv[4], vv[5], vv[6], vv[7]});
-  st_stream<ntw>((u32x2*)(A.pout + oa), u32x2{bf16_pack2(th[0], th[1]), bf16_pack2(th[2], th[3])});
-  st_stream<ntw>((u32x2*)(A.pout + ob), u32x2{bf16_pack2(th[4], th[5]), bf16_pack2(th[6], th[7])});
+#pragma unroll
+  for (int k = 0; k < NPC; ++k) st_stream<ntw>((f32x4*)(A.master + ip[k]), th[k]);
+#pragma unroll
+  for (int k = 0; k < NPC; ++k) st_stream<ntw>((f32x4*)(A.m + ip[k]), mm[k]);
+#pragma unroll
+  for (int k = 0; k < NPC; ++k) st_stream<ntw>((f32x4*)(A.v + ip[k]), vv[k]);
+#pragma unroll
+  for (int k = 0; k < NPC; ++k)
+    st_stream<ntw>((u32x2*)(A.pout + op[k]),
+                   u32x2{bf16_pack2(th[k].x, th[k].y), bf16_pack2(th[k].z, th[k].w)});
   if (A.gout) {
-    st_stream<ntw>((f32x4*)(A.gout + ia), f32x4{g[0], g[1], g[2], g[3]});
-    st_stream<ntw>((f32x4*)(A.gout + ib), f32x4{g[4], g[5], g[6], g[7]});
+#pragma unroll
+    for (int k = 0; k < NPC; ++k) st_stream<ntw>((f32x4*)(A.gout + ip[k]), g[k]);
   }
 }
 
@@ -316,46 +344,56 @@ __device__ __forceinline__ void advance(int64_t& b, int64_t& j, int64_t adv, int
   }
 }
 
-// Vector path over one Region, grid-stride over chunks of 512 elements: in
-// each chunk, lane l of a wave takes the 4-element pieces at 4l and 256 + 4l,
-// so that every load and store instruction of the wave covers one
-// contiguous span (1 KB of fp32, 512 bytes of bf16) and each cache line is
-// fetched by one instruction.  Requires 16-byte aligned bases and
-// i0 % 4 == 0; when mapping, flat0 % 4 == 0 and (part 0 is one bucket, or
-// seg % 4 == 0 and pstride % 4 == 0), and if part 1 exists n0 % 4 == 0 and
-// flat1 % 4 == 0, so that no piece straddles a bucket and every piece
+// Vector path over one Region, grid-stride over chunks of 512*NPAIR
+// elements per wave: in each chunk, lane l takes the 4-element pieces at
+// 256*k + 4l (k < 2*NPAIR), so that every load and store instruction of the
+// wave covers one contiguous span (1 KB of fp32, 512 bytes of bf16) and each
+// cache line is fetched by one instruction.  Requires 16-byte aligned bases
+// and i0 % 4 == 0; when mapping, flat0 % 4 == 0 and (part 0 is one bucket,
+// or seg % 4 == 0 and pstride % 4 == 0), and if part 1 exists n0 % 4 == 0
+// and flat1 % 4 == 0, so that no piece straddles a bucket and every piece
 // address is aligned.  The elements after the last full chunk run one per
 // thread.
-template <int ND, bool MAP, int GROUP, int NT, int GT>
+template <int ND, bool MAP, int GROUP, int NT, int GT, int NPAIR>
 __global__ void __launch_bounds__(256) step_vec_kernel(const ArgsFor<ND, GT> A) {
+  static_assert(NPAIR == 1 || NPAIR == 2 || NPAIR == 4, "chunk of 512, 1024 or 2048 elements");
+  constexpr int NPC = 2 * NPAIR;
+  constexpr int LOG_CH = NPAIR == 1 ? 9 : (NPAIR == 2 ? 10 : 11);
   const Region& R = A.reg;
   const int64_t n = R.n;
-  const int64_t nchunk = n >> 9;
+  const int64_t nchunk = n >> LOG_CH;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t T = (int64_t)gridDim.x * blockDim.x;
-  const int64_t wave = tid >> 6, W = T >> 6, adv = W << 9;
-  int64_t ea = (wave << 9) + ((threadIdx.x & 63) << 2);
-  int64_t ba = 0, ja = 0, bb = 0, jb = 0;
-  if (MAP) {
-    ba = ea / R.seg;
-    ja = ea - ba * R.seg;
-    bb = (ea + 256) / R.seg;
-    jb = ea + 256 - bb * R.seg;
-  }
-  for (int64_t c = wave; c < nchunk; c += W, ea += adv) {
-    const int64_t eb = ea + 256;
-    const int64_t ia = R.i0 + ea, ib = R.i0 + eb;
-    int64_t fa = ia, fb = ib;
+  const int64_t wave = tid >> 6, W = T >> 6, adv = W << LOG_CH;
+  int64_t e0 = (wave << LOG_CH) + ((threadIdx.x & 63) << 2);
+  int64_t bk[NPC], jk[NPC];
+#pragma unroll
+  for (int k = 0; k < NPC; ++k) {
+    bk[k] = 0;
+    jk[k] = 0;
     if (MAP) {
-      fa = ea < R.n0 ? R.flat0 + ba * R.pstride + ja : R.flat1 + (ea - R.n0);
-      fb = eb < R.n0 ? R.flat0 + bb * R.pstride + jb : R.flat1 + (eb - R.n0);
-      advance(ba, ja, adv, R.seg);
-      advance(bb, jb, adv, R.seg);
+      bk[k] = (e0 + 256 * k) / R.seg;
+      jk[k] = e0 + 256 * k - bk[k] * R.seg;
     }
-    const bool fg = MAP && A.flat_grad, so = MAP && A.slot_out;
-    step8<ND, GROUP, NT, GT>(A, ia, fg ? fa : ia, so ? fa : ia, ib, fg ? fb : ib, so ? fb : ib);
   }
-  for (int64_t e = (nchunk << 9) + tid; e < n; e += T) step_one<GT>(A, e, MAP);
+  const bool fg = MAP && A.flat_grad, so = MAP && A.slot_out;
+  for (int64_t c = wave; c < nchunk; c += W, e0 += adv) {
+    int64_t ip[NPC], gp[NPC], op[NPC];
+#pragma unroll
+    for (int k = 0; k < NPC; ++k) {
+      const int64_t e = e0 + 256 * k;
+      ip[k] = R.i0 + e;
+      int64_t f = ip[k];
+      if (MAP) {
+        f = e < R.n0 ? R.flat0 + bk[k] * R.pstride + jk[k] : R.flat1 + (e - R.n0);
+        advance(bk[k], jk[k], adv, R.seg);
+      }
+      gp[k] = fg ? f : ip[k];
+      op[k] = so ? f : ip[k];
+    }
+    step_pieces<ND, GROUP, NT, GT, NPAIR>(A, ip, gp, op);
+  }
+  for (int64_t e = (nchunk << LOG_CH) + tid; e < n; e += T) step_one<GT>(A, e, MAP);
 }
 
 // Many single-bucket regions in one launch (the per-parameter layout, where
@@ -416,7 +454,8 @@ __global__ void __launch_bounds__(256) step_table_kernel(const ArgsFor<ND, GT> A
     const int64_t ga = A.flat_grad ? fa : ia, oa = A.slot_out ? fa : ia;
     const int64_t gb = A.flat_grad ? fb : ib, ob = A.slot_out ? fb : ib;
     if (T.vec_ok && ((r0 | f0) & 3) == 0 && eb + 4 <= n) {
-      step8<ND, GROUP, NT, GT>(A, ia, ga, oa, ib, gb, ob);
+      const int64_t ip[2] = {ia, ib}, gp[2] = {ga, gb}, op[2] = {oa, ob};
+      step_pieces<ND, GROUP, NT, GT, 1>(A, ip, gp, op);
     } else {
       const int64_t ma = n - ea < 4 ? n - ea : 4;
       for (int64_t e = 0; e < ma; ++e) step_at<GT>(A, ia + e, ga + e, oa + e);
@@ -485,15 +524,11 @@ int cu_count() {
   return n;
 }
 
-// Launch policy, from measurements on MI355X (Llama-3-8B shard, N_d = 8,
-// buffers placed by zero_placement_plan):
-//   read-dominated (64 or more bytes of contributions per element):
-//     non-temporal accesses, one 256-thread block per CU;
-//   bf16 contributions otherwise: ordinary accesses, two 128-thread blocks
-//     per CU (7.00 ms against 7.07 with two 256-thread blocks);
-//   fp32 contributions: ordinary accesses, two 256-thread blocks per CU;
-//   accumulator + last micro-batch: ordinary accesses, one 256-thread block
-//     per CU (12.6 ms against 13.2 with two).
+// Launch policy, from measurements on MI355X (Llama-3-8B and Llama-70B
+// shards, buffers placed by zero_placement_plan): one 256-thread block per
+// CU, except two 128-thread blocks per CU for fp32 contributions that are
+// not read-dominated (64 or more bytes of contributions per element); the
+// cache policy and the chunk size below.
 constexpr bool read_dominated(int nd, int gt) { return nd * contrib_bytes(gt) >= 64; }
 // Cache policy, measured on the tuned llama8b / llama70b buffers (every
 // policy and launch shape, N_d = 8 to 64): with each cache line fetched by a
@@ -506,6 +541,17 @@ constexpr int cache_policy(int nd, int gt) {
   return (gt == GT_BF16 || read_dominated(nd, gt)) ? NT_CONTRIB | NT_STATE | NT_STORE
                                                    : NT_CONTRIB;
 }
+// Pairs of 4-element pieces per lane and chunk of the vector kernel, and
+// the ranks whose loads are in flight together.  Measured on the tuned
+// llama8b / llama70b buffers (same pool, library builds timed alternately):
+// at N_d = 64 with bf16 contributions, chunks of 1024 elements per wave
+// (each rank's run 2 KB per wave) with 8 ranks in flight take 28.76 ms
+// against 29.05 ms for 512-element chunks with 16 ranks; at N_d = 8 the two
+// are equal (6.74 ms) and 2048-element chunks are slower (10.8 ms).  The
+// fused loads are 12 dwords per rank: 8 ranks in flight, or they spill at
+// N_d = 64.
+constexpr int step_pairs(int nd, int gt) { return (gt == GT_BF16 && nd >= 64) ? 2 : 1; }
+constexpr int step_group_max(int gt, int pairs) { return (fused(gt) || pairs > 1) ? 8 : 16; }
 struct Policy {
   int blocks_per_cu, threads;
 };
@@ -549,9 +595,9 @@ template <int ND, int GT, int KIND, int NT>
 int launch_nt(const Call& c, const Work& w, hipStream_t s) {
   ArgsFor<ND, GT> A;
   fill_args(A, c, w.reg ? *w.reg : Region{0, 0, 0, 1, 0, 0, 0});
-  // ranks whose loads are in flight together: 16 (8 for the 12-dword fused
-  // loads, which would otherwise spill at N_d = 64)
-  constexpr int GMAX = fused(GT) ? 8 : 16;
+  // the table kernel takes one pair per lane
+  constexpr int NPAIR = KIND == K_TABLE ? 1 : step_pairs(ND, GT);
+  constexpr int GMAX = step_group_max(GT, NPAIR);
   constexpr int GROUP = ND > GMAX ? GMAX : (ND > 1 ? ND - 1 : 1);
   if constexpr (KIND == K_TABLE) {
     using Tab = TableFor<ND, GT>;
@@ -570,8 +616,8 @@ int launch_nt(const Call& c, const Work& w, hipStream_t s) {
     hipLaunchKernelGGL((step_table_kernel<ND, GROUP, NT, GT>), dim3(w.blocks), dim3(w.threads), 0,
                        s, A, T);
   } else {
-    hipLaunchKernelGGL((step_vec_kernel<ND, KIND == K_MAP, GROUP, NT, GT>), dim3(w.blocks),
-                       dim3(w.threads), 0, s, A);
+    hipLaunchKernelGGL((step_vec_kernel<ND, KIND == K_MAP, GROUP, NT, GT, NPAIR>),
+                       dim3(w.blocks), dim3(w.threads), 0, s, A);
   }
   return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP;
 }

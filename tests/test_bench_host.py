@@ -19,11 +19,11 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_step_kernel_names_follow_the_launch_policy():
-    assert bench.step_kernel_name(8, True) == "step_vec_kernel<8, true, 7, 7, 0>"
-    assert bench.step_kernel_name(64, False) == "step_vec_kernel<64, false, 16, 7, 0>"
-    assert bench.step_kernel_name(4, True) == "step_vec_kernel<4, true, 3, 7, 0>"
-    assert bench.step_kernel_name(32, False) == "step_vec_kernel<32, false, 16, 7, 0>"
-    assert bench.step_kernel_name(100, True) == "step_vec_kernel<0, true, 1, 7, 0>"
+    assert bench.step_kernel_name(8, True) == "step_vec_kernel<8, true, 7, 7, 0, 1>"
+    assert bench.step_kernel_name(64, False) == "step_vec_kernel<64, false, 8, 7, 0, 2>"
+    assert bench.step_kernel_name(4, True) == "step_vec_kernel<4, true, 3, 7, 0, 1>"
+    assert bench.step_kernel_name(32, False) == "step_vec_kernel<32, false, 16, 7, 0, 1>"
+    assert bench.step_kernel_name(100, True) == "step_vec_kernel<0, true, 1, 7, 0, 1>"
 
 
 def test_traffic_is_reported_only_for_the_profiled_sources(tmp_path, monkeypatch):

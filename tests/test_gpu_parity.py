@@ -235,6 +235,11 @@ EDGE = [
     ([65536 + 13], 0, 32, 31, "flat", "ag_slot"),
     ([64 * 300 + 1], 6400, 64, 63, "compact", "shard"),     # N_d = 64 with padded tails
     ([64 * 300 + 1], 6400, 64, 0, "flat", "ag_slot"),
+    # N_d = 64 runs chunks of 1024 elements per wave: slices of 1040 make the
+    # chunks cross bucket cuts, a 2-element last slice runs element-wise
+    ([64 * 1040 * 6 + 70], 64 * 1040, 64, 63, "flat", "ag_slot"),
+    ([64 * 1040 * 6 + 70], 64 * 1040, 64, 5, "compact", "ag_slot"),
+    ([64 * 5003], 0, 64, 17, "compact", "shard"),         # 4 full chunks + 907 tail
     ([100 * 97], 0, 100, 99, "compact", "shard"),           # generic rank count
     ([256 * 33 + 7], 0, 256, 255, "flat", "ag_slot"),       # largest rank count
     ([8], 0, 8, 5, "flat", "ag_slot"),                      # one element per rank
@@ -376,6 +381,24 @@ def test_launch_shape_invariance(launch):
         case.init_state_gpu()
         grads = case.grads_gpu(5)
         case.step_gpu(5, grads, launch=lc)
+        torch.cuda.synchronize()
+        outs.append([case.master.cpu().numpy(), case.m.cpu().numpy(), case.v.cpu().numpy(),
+                     u16(case.pout), case.gout.cpu().numpy()])
+    for a, b in zip(*outs):
+        assert_bitwise(a, b, f"launch {launch}")
+
+
+@pytest.mark.parametrize("launch", [(1, 64, 0), (13, 192, 0), (3000, 128, 0), (0, 0, 1)])
+def test_launch_shape_invariance_at_64_ranks(launch):
+    """The same at N_d = 64, whose vector kernel takes 1024-element chunks
+    per wave: bit-identical for any grid / block size and the scalar path."""
+    numel, cap, n_d, rank = [64 * 1040 * 9 + 200, 64 * 77], 64 * 1040, 64, 62
+    outs = []
+    for lc in (None, launch):
+        case = _edge_case(numel, cap, n_d, rank, "flat", "ag_slot")
+        case.init_state_gpu()
+        grads = case.grads_gpu(4)
+        case.step_gpu(4, grads, launch=lc)
         torch.cuda.synchronize()
         outs.append([case.master.cpu().numpy(), case.m.cpu().numpy(), case.v.cpu().numpy(),
                      u16(case.pout), case.gout.cpu().numpy()])
