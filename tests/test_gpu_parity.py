@@ -635,6 +635,7 @@ BUCKET_RANGES = [
     ([64 * 300 + 1], 6400, 64, 63, "flat", "ag_slot"),
     ([8192 * 6], 8192, 8, 2, "flat", "ag_slot"),            # six equal buckets
     ([100 * 97], 1000, 100, 99, "compact", "shard"),         # runtime rank count
+    ([64 * 1040 * 6 + 70], 64 * 1040, 64, 63, "flat", "ag_slot"),  # 1024-element chunks
 ]
 
 
@@ -1249,6 +1250,7 @@ DIM0_EDGE = [
     ([(100, 24), (3, 8), (64, 64)], 8, 7, "flat", "shard"),
     ([(129, 64), (1000,)], 64, 63, "compact", "shard"),
     ([(129, 64), (1000,), (2, 3)], 64, 5, "flat", "ag_slot"),
+    ([(64 * 40, 48), (1000,)], 64, 63, "compact", "shard"),   # 1024-element chunks + tail
     ([(33, 17), (1,), (250, 40)], 3, 2, "flat", "ag_slot"),
     # 75 tensors: three table launches mixing aligned and unaligned slices
     ([((k * 7) % 41 + 1, (k * 5) % 13 + 1) if k % 9 else (64, 64) for k in range(75)],
