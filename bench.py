@@ -242,7 +242,8 @@ def make_timer(stream):
 
 
 def aux_kernels(z, synth, workloads, placement):
-    """Pack (gpt2s list, one rank's 124M-element flat buffer), the no_sync
+    """Pack (gpt2s list, one rank's 124M-element flat buffer), the gpt2s
+    launch sequence (8 ranks pack, then the step), the no_sync
     accumulate sequence (accum1p3b shard: 4 calls for one rank) and the whole
     accum1p3b job (8 ranks accumulate, then the step; the last accumulate
     separate or folded into the step), timed with HIP events.  With a pool
@@ -280,6 +281,36 @@ def aux_kernels(z, synth, workloads, placement):
         synth.fill_device(v[f"t{k}"], segs, synth.key(w.name, "grad", 0, 0, 1), *w.grad)
     record("pack_kernel", "gpt2s: 148 tensors -> 124,439,808-element flat buffer, 25 MiB "
            "buckets", 2 * L.psi + 2 * L.padded, timed(lambda: pack(v)))
+    del v
+    torch.cuda.empty_cache()
+
+    # the gpt2s launch sequence of one optimizer step: every simulated rank
+    # packs its own 148 tensors into its flat bucket buffer, then the step
+    # reads rank r's slice of each bucket from the 8 buffers (FLAT) and
+    # writes the All-Gather slots
+    nd = w.n_d
+    hp = z.AdamW(**w.hp)
+    specs = [(f"t{q}_{k}", n, torch.int16, float(n)) for q in range(nd)
+             for k, n in enumerate(w.numel)]
+    specs += [(f"flat{q}", L.padded, torch.int16, float(L.padded)) for q in range(nd)]
+    specs += [(k, L.shard, torch.float32, 8.0) for k in ("master", "exp_avg", "exp_avg_sq")]
+    specs += [("param_out", L.padded, torch.int16, 2.0)]
+
+    def gpt2s_job(v):
+        for q in range(nd):
+            z.zero_bucket_pack(L, [v[f"t{q}_{k}"] for k in range(nt)], v[f"flat{q}"])
+        z.zero_shard_step(L, hp, w.t_first, [v[f"flat{q}"] for q in range(nd)], z.GRAD_FLAT,
+                          v["master"], v["exp_avg"], v["exp_avg_sq"], v["param_out"],
+                          z.OUT_AG_SLOT)
+
+    v = buffers(specs, gpt2s_job)
+    tsegs = synth.tensor_segments(w.numel)
+    for q in range(nd):
+        for k, segs in enumerate(tsegs):
+            synth.fill_device(v[f"t{q}_{k}"], segs, synth.key(w.name, "grad", q, 0, 1), *w.grad)
+    record("pack_kernel x8 + step_vec_kernel", f"gpt2s step: {nd} ranks pack 148 tensors each, "
+           "then the shard step on rank 7's slices (FLAT, AG slot)",
+           nd * (2 * L.psi + 2 * L.padded) + L.shard * (2 * nd + 26), timed(lambda: gpt2s_job(v)))
     del v
     torch.cuda.empty_cache()
 
