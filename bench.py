@@ -87,6 +87,10 @@ class Inputs:
 
 
 TUNE_SLACK = 32 << 30   # extra pool bytes over which the tuned placement may shift
+# the main workload's pool: (spare bytes, shift step) tried in order until one
+# fits; within a pool of 200+ GiB the fastest starts lie further in (llama8b:
+# 6.67 ms at 88 GiB against 6.73 ms within the first 32 GiB)
+MAIN_TUNE = ((128 << 30, 8 << 30), (32 << 30, 4 << 30))
 
 
 def step_call(z, L, hp, t, grad_layout, out_mode, fused=False):
@@ -104,14 +108,15 @@ def step_call(z, L, hp, t, grad_layout, out_mode, fused=False):
 
 
 def make_inputs(z, synth, w, L, placement="tuned", grad_dtype=None, accumulators=False,
-                grad_micro=0, call=None):
+                grad_micro=0, call=None, tune=((TUNE_SLACK, 4 << 30),)):
     """Buffers for workload w on layout L filled with the workload's seeded
     values (contributions keyed (grad, rank, grad_micro, t_first); FLAT ones
     over the padded flat buffer), the output zeroed.  placement "tuned": one
-    pool laid out by zero_placement_plan with TUNE_SLACK spare bytes, the
-    arrangement's start chosen by timing `call` (views -> one call) at 4 GiB
-    shifts; "planned": the same pool without spare bytes; "separate": one
-    torch allocation per buffer."""
+    pool laid out by zero_placement_plan with spare bytes, the arrangement's
+    start chosen by timing `call` (views -> one call) at shifts over the
+    spare room (`tune`: (spare bytes, shift step) pairs tried in order until
+    a pool fits); "planned": the same pool without spare bytes; "separate":
+    one torch allocation per buffer."""
     import torch
     from fsdp_sharded_optimizer_step_amd import placement as zp
     dev = torch.device("cuda:0")
@@ -130,14 +135,19 @@ def make_inputs(z, synth, w, L, placement="tuned", grad_dtype=None, accumulators
                 call = step_call(z, L, z.AdamW(**w.hp), w.t_first, gl, om, fused=accumulators)
             timed = make_timer(torch.cuda.current_stream())
             choose = lambda v: timed(lambda: call(v), reps=4)
-        try:
-            pool = zp.Pool(specs, device=dev, slack=TUNE_SLACK if placement == "tuned" else 0,
-                           choose=choose)
-            views = pool.views
-        except torch.cuda.OutOfMemoryError:
+        tries = tune if placement == "tuned" else ((0, 4 << 30),)
+        for slack, step in tries:
+            try:
+                pool = zp.Pool(specs, device=dev, slack=slack, choose=choose, shift_step=step)
+                views = pool.views
+                break
+            except torch.cuda.OutOfMemoryError:
+                torch.cuda.empty_cache()
+                print(f"# {placement} pool with {slack >> 30} GiB spare does not fit",
+                      file=sys.stderr, flush=True)
+        if pool is None:
             # a device without room for the pool's spare lanes: one
             # allocation per buffer instead (reported as such)
-            torch.cuda.empty_cache()
             print(f"# {placement} pool does not fit; separate allocations", file=sys.stderr,
                   flush=True)
             placement = "separate"
@@ -500,7 +510,7 @@ def all_configs(z, synth, workloads, steps, warmup, placement):
         w = workloads.get(name)
         L = z.Layout(w.numel, w.cap, w.n_d, w.rank, rows=w.rows)
         S = L.shard
-        inp, _ = make_inputs(z, synth, w, L, placement)
+        inp, _ = make_inputs(z, synth, w, L, placement, tune=MAIN_TUNE)
         hp = z.AdamW(**w.hp)
         gl = z.GRAD_COMPACT if w.grad_layout == "compact" else z.GRAD_FLAT
         om = z.OUT_AG_SLOT if w.out_mode == "ag_slot" else z.OUT_SHARD
@@ -592,7 +602,7 @@ def main():
     S, P = L.shard, L.padded
     print(f"# workload {w.name}: S={S} P={P} N_d={w.n_d} buckets={L.n_buckets}", file=sys.stderr,
           flush=True)
-    inp, segs = make_inputs(z, synth, w, L, args.placement)
+    inp, segs = make_inputs(z, synth, w, L, args.placement, tune=MAIN_TUNE)
     placement_used = "separate" if inp.pool is None else args.placement
     hp = z.AdamW(**w.hp)
     gl = z.GRAD_COMPACT if w.grad_layout == "compact" else z.GRAD_FLAT
