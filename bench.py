@@ -90,7 +90,7 @@ TUNE_SLACK = 32 << 30   # extra pool bytes over which the tuned placement may sh
 # the main workload's pool: (spare bytes, shift step) tried in order until one
 # fits; within a pool of 200+ GiB the fastest starts lie further in (llama8b:
 # 6.67 ms at 88 GiB against 6.73 ms within the first 32 GiB)
-MAIN_TUNE = ((128 << 30, 8 << 30), (32 << 30, 4 << 30))
+MAIN_TUNE = ((128 << 30, 8 << 30), (64 << 30, 8 << 30), (32 << 30, 4 << 30))
 
 
 def step_call(z, L, hp, t, grad_layout, out_mode, fused=False):
@@ -470,7 +470,7 @@ def next_rows(z, synth, w, L, holder, timed, placement):
     del inp, shard_out, dst16
     torch.cuda.empty_cache()
     # fp32 contributions
-    inp, _ = make_inputs(z, synth, w, L, placement, grad_dtype=torch.float32)
+    inp, _ = make_inputs(z, synth, w, L, placement, grad_dtype=torch.float32, tune=MAIN_TUNE)
     ms = timed(lambda: z.zero_shard_step(L, hp, 7, inp.grads, z.GRAD_COMPACT, *inp.state,
                                          inp.pout, z.OUT_AG_SLOT))
     row("step_f32", "step_vec_kernel (fp32 contributions)", "llama8b with fp32 contributions "
@@ -479,7 +479,8 @@ def next_rows(z, synth, w, L, holder, timed, placement):
     torch.cuda.empty_cache()
     # the last no_sync micro-batch folded into the step: each rank's fp32
     # accumulator plus its bf16 micro-batch
-    inp, _ = make_inputs(z, synth, w, L, placement, accumulators=True, grad_micro=1)
+    inp, _ = make_inputs(z, synth, w, L, placement, accumulators=True, grad_micro=1,
+                         tune=MAIN_TUNE)
     ms = timed(lambda: z.zero_shard_step_accumulate(L, hp, 8, inp.accs, inp.grads, 0.25,
                                                     z.DTYPE_BF16, z.GRAD_COMPACT, *inp.state,
                                                     inp.pout, z.OUT_AG_SLOT))
