@@ -59,6 +59,8 @@ def _load():
         C.c_double] * 5 + [C.c_int64, _f32p, _f32p, _f32p, _u16p, _f32p, C.c_int32]
     lib.oracle_model_state_bytes.argtypes = [C.c_int32, C.c_int64, C.c_int64, C.c_int32]
     lib.oracle_model_state_bytes.restype = C.c_double
+    lib.oracle_comm_bytes_per_gpu.argtypes = [C.c_int32, C.c_int64, C.c_int32]
+    lib.oracle_comm_bytes_per_gpu.restype = C.c_double
     for name in ("oracle_plan_counts", "oracle_plan_buckets", "oracle_plan_tensor_ranges",
                  "oracle_plan_map", "oracle_pack", "oracle_slice", "oracle_gather",
                  "oracle_plan_locate", "oracle_reshard", "oracle_shard_step",
@@ -291,3 +293,12 @@ MODES = {"baseline": 0, "zero1": 1, "zero2": 2, "zero3": 3}
 
 def model_state_bytes(mode: str, P: int, S: int, k: int = 12) -> float:
     return _load().oracle_model_state_bytes(MODES[mode], P, S, k)
+
+
+COMM_MODES = {"ddp": 0, "zero1": 1, "zero2": 2, "zero3": 3}
+
+
+def comm_bytes_per_gpu(mode: str, P: int, n_d: int) -> float:
+    """Bytes one GPU sends per training step under the ring model (16-bit
+    parameters and gradients over a P-element padded layout)."""
+    return _load().oracle_comm_bytes_per_gpu(COMM_MODES[mode], P, n_d)

@@ -526,4 +526,21 @@ double oracle_model_state_bytes(int32_t mode, int64_t P, int64_t S, int32_t k_by
   return params + grads + state;
 }
 
+// [DP] "Zero Redundancy Optimizer (ZeRO)", communication-volume discussion:
+// bytes one GPU sends per training step (one forward and one backward) under
+// the ring model, parameters and gradients 16-bit, summed over every layer or
+// bucket.  A ring Reduce-Scatter or All-Gather of a P-element buffer has each
+// rank send N_d - 1 chunks of P / N_d elements; an All-Reduce is one of each.
+//   mode 0 (naive DP): one gradient All-Reduce
+//   mode 1, 2 (ZeRO-1, ZeRO-2): gradient Reduce-Scatter + parameter All-Gather
+//   mode 3 (ZeRO-3): parameter All-Gather before forward and again before
+//     backward, plus the gradient Reduce-Scatter
+// Pinned by: a ring simulation that moves the data and counts the bytes, and
+// the page's 4 Psi / 4 Psi / 6 Psi once the (N_d - 1) / N_d factor is dropped.
+double oracle_comm_bytes_per_gpu(int32_t mode, int64_t P, int32_t n_d) {
+  const double pass = 2.0 * (double)P * (double)(n_d - 1) / (double)n_d;  // one RS or AG
+  const int passes = mode >= 3 ? 3 : 2;
+  return pass * (double)passes;
+}
+
 }  // extern "C"

@@ -78,6 +78,11 @@ MUTATIONS = [
     ("ZeRO-1 state counted unsharded",
      "double state = (double)k_bytes * (double)((mode >= 1) ? S : P);",
      "double state = (double)k_bytes * (double)((mode >= 2) ? S : P);", False),
+    ("ZeRO-3 counts one parameter All-Gather", "const int passes = mode >= 3 ? 3 : 2;",
+     "const int passes = mode >= 3 ? 2 : 2;", False),
+    ("ring pass without the (N_d - 1) / N_d factor",
+     "const double pass = 2.0 * (double)P * (double)(n_d - 1) / (double)n_d;",
+     "const double pass = 2.0 * (double)P;", False),
 ]
 
 
@@ -109,6 +114,8 @@ def pin_calls(with_exhaustive: bool):
     calls += [(P.test_layout_workload_sizes_closed_form, {"name": n}) for n in workloads.NAMES]
     calls += [(P.test_layout_padded_tail_workload, {})]
     calls += [(P.test_memory_formulas, {"name": n}) for n in workloads.NAMES]
+    calls += [(P.test_comm_volume_ring_simulation, {"n_d": n}) for n in (1, 2, 3, 4, 5, 8)]
+    calls += [(P.test_comm_volume_closed_forms, {"name": n}) for n in workloads.NAMES]
     if with_exhaustive:
         calls += [(P.test_bf16_round_exhaustive_vs_torch, {})]
     return calls

@@ -629,3 +629,81 @@ def test_memory_formulas(name):
     assert oracle.model_state_bytes("zero2", P, S) == 2 * P + (2 * P + k * P) / N
     assert oracle.model_state_bytes("zero3", P, S) == (2 * P + 2 * P + k * P) / N
 
+
+
+# ------------------------------------------------------------------ communication volumes
+def _ring_reduce_scatter(bufs):
+    """A ring Reduce-Scatter played step by step: every rank's buffer is cut
+    into N chunks; in step s, rank r sends its running copy of chunk
+    (r - s) mod N to rank r + 1, which adds it to its own copy.  Returns, per
+    rank, (the chunk it ends with, that chunk's index) and the bytes each rank
+    sent with 2-byte elements."""
+    n = len(bufs)
+    c = len(bufs[0]) // n
+    cur = [[list(b[k * c:(k + 1) * c]) for k in range(n)] for b in bufs]
+    sent = [0] * n
+    for s in range(n - 1):
+        msgs = [(r, (r - s) % n, list(cur[r][(r - s) % n])) for r in range(n)]
+        for r, k, data in msgs:
+            sent[r] += 2 * len(data)
+            dst = (r + 1) % n
+            cur[dst][k] = [a + b for a, b in zip(cur[dst][k], data)]
+    return [(cur[r][(r + 1) % n], (r + 1) % n) for r in range(n)], sent
+
+
+def _ring_all_gather(owned):
+    """A ring All-Gather played step by step: rank r starts with chunk
+    owned[r] = (data, index); in step s it forwards the chunk it received in
+    step s - 1 (its own in step 0) to rank r + 1.  Returns every rank's
+    assembled buffer and the bytes each rank sent with 2-byte elements."""
+    n = len(owned)
+    have = [{k: list(d)} for d, k in owned]
+    last = [k for _, k in owned]
+    sent = [0] * n
+    for _ in range(n - 1):
+        msgs = [(r, last[r], have[r][last[r]]) for r in range(n)]
+        for r, k, data in msgs:
+            sent[r] += 2 * len(data)
+            dst = (r + 1) % n
+            have[dst][k] = list(data)
+            last[dst] = k
+    full = [[x for k in range(n) for x in have[r][k]] for r in range(n)]
+    return full, sent
+
+
+@pytest.mark.parametrize("n_d", [1, 2, 3, 4, 5, 8])
+def test_comm_volume_ring_simulation(n_d):
+    """Bytes one GPU sends per step equal those of a played-out ring: naive
+    DP All-Reduces the gradients (Reduce-Scatter + All-Gather), ZeRO-1/2
+    Reduce-Scatter the gradients and All-Gather the updated parameters,
+    ZeRO-3 All-Gathers the parameters twice (forward, backward) and
+    Reduce-Scatters the gradients.  The played ring also has to compute the
+    right results."""
+    rng = np.random.default_rng(n_d)
+    P = n_d * 6
+    bufs = [rng.integers(-50, 50, P).tolist() for _ in range(n_d)]
+    total = [sum(b[i] for b in bufs) for i in range(P)]
+    c = P // n_d
+    reduced, sent_rs = _ring_reduce_scatter(bufs)
+    assert sorted(k for _, k in reduced) == list(range(n_d))
+    for chunk, k in reduced:
+        assert chunk == total[k * c:(k + 1) * c]
+    full, sent_ag = _ring_all_gather(reduced)
+    assert all(f == total for f in full)
+    assert len(set(sent_rs)) == 1 and len(set(sent_ag)) == 1
+    rs, ag = sent_rs[0], sent_ag[0]
+    assert oracle.comm_bytes_per_gpu("ddp", P, n_d) == rs + ag
+    assert oracle.comm_bytes_per_gpu("zero1", P, n_d) == rs + ag
+    assert oracle.comm_bytes_per_gpu("zero2", P, n_d) == rs + ag
+    assert oracle.comm_bytes_per_gpu("zero3", P, n_d) == rs + 2 * ag
+
+
+@pytest.mark.parametrize("name", workloads.NAMES)
+def test_comm_volume_closed_forms(name):
+    """Dropping the (N_d - 1) / N_d factor gives the page's 4 Psi (naive DP,
+    ZeRO-1, ZeRO-2) and 6 Psi (ZeRO-3), with Psi -> P (padded)."""
+    w = workloads.get(name)
+    P = oracle.plan(w.numel, w.cap, w.n_d).padded_total
+    f = w.n_d / (w.n_d - 1)
+    for mode, k in (("ddp", 4), ("zero1", 4), ("zero2", 4), ("zero3", 6)):
+        assert oracle.comm_bytes_per_gpu(mode, P, w.n_d) * f == pytest.approx(k * P, rel=1e-12)
