@@ -428,6 +428,13 @@ def next_rows(z, synth, w, L, holder, timed, placement):
                                          shard_out, z.OUT_SHARD))
     row("fsdp2_step", "step_vec_kernel", "llama8b_fsdp2: Llama-3-8B per-parameter dim-0 "
         "layout, N_d=8, rank 7, in place", S * (2 * w.n_d + 26), ms)
+    # the same layout with All-Gather slot output: every tensor's slice has
+    # its own slot, so the step runs as table launches
+    assert Ld.padded == P
+    ms = timed(lambda: z.zero_shard_step(Ld, hp, 5, inp.grads, z.GRAD_COMPACT, *inp.state,
+                                         inp.pout, z.OUT_AG_SLOT))
+    row("fsdp2_step_slot", "step_table_kernel", "llama8b_fsdp2 with All-Gather slot output: "
+        "291 per-tensor slots, 2 table launches", S * (2 * w.n_d + 26), ms)
     # ZeRO-2 stepping bucket by bucket (as each bucket's Reduce-Scatter
     # lands): the same update as one call per bucket range, captured in a
     # HIP graph so that the host's launch rate is not what is timed

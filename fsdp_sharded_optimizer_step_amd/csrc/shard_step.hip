@@ -272,6 +272,57 @@ __device__ __forceinline__ void step_at(const Args& A, int64_t i, int64_t gi, in
   if (A.gout) A.gout[i] = g;
 }
 
+// Up to 8 elements in two pieces (piece k: cnt[k] <= 4 consecutive elements
+// from shard index i[k], contribution index gi[k], output index oi[k]), the
+// arithmetic of step_at with every load issued before the first store, so
+// that a lane waits for memory once rather than once per element: the ends
+// of table regions, where a tile holds only part of a chunk.
+template <int ND, int GT, class Args>
+__device__ __forceinline__ void step_upto8(const Args& A, const int64_t (&i)[2],
+                                           const int64_t (&gi)[2], const int64_t (&oi)[2],
+                                           const int (&cnt)[2]) {
+  float a[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    a[e] = (e & 3) < cnt[e >> 2] ? load_one<GT>(A, 0, gi[e >> 2] + (e & 3)) : 0.0f;
+  if constexpr (ND > 0) {
+    constexpr int kUnroll = ND <= 16 ? ND : 4;
+#pragma unroll kUnroll
+    for (int q = 1; q < ND; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if ((e & 3) < cnt[e >> 2]) a[e] = a[e] + load_one<GT>(A, q, gi[e >> 2] + (e & 3));
+  } else {
+    for (int q = 1; q < A.nd; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if ((e & 3) < cnt[e >> 2]) a[e] = a[e] + load_one<GT>(A, q, gi[e >> 2] + (e & 3));
+  }
+  float th[8], m[8], v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if ((e & 3) < cnt[e >> 2]) {
+      const int64_t x = i[e >> 2] + (e & 3);
+      th[e] = A.master[x];
+      m[e] = A.m[x];
+      v[e] = A.v[x];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if ((e & 3) < cnt[e >> 2]) {
+      const int64_t x = i[e >> 2] + (e & 3);
+      const float g = average<0>(a[e], A);
+      adamw(g, th[e], m[e], v[e], A.k);
+      A.master[x] = th[e];
+      A.m[x] = m[e];
+      A.v[x] = v[e];
+      A.pout[oi[e >> 2] + (e & 3)] = (uint16_t)bf16_round(th[e]);
+      if (A.gout) A.gout[x] = g;
+    }
+  }
+}
+
 // Element e of the launch's Region, generic addressing (tails, scalar path).
 template <int GT, class Args>
 __device__ __forceinline__ void step_one(const Args& A, int64_t e, bool map) {
@@ -457,10 +508,10 @@ __global__ void __launch_bounds__(256) step_table_kernel(const ArgsFor<ND, GT> A
       const int64_t ip[2] = {ia, ib}, gp[2] = {ga, gb}, op[2] = {oa, ob};
       step_pieces<ND, GROUP, NT, GT, 1>(A, ip, gp, op);
     } else {
-      const int64_t ma = n - ea < 4 ? n - ea : 4;
-      for (int64_t e = 0; e < ma; ++e) step_at<GT>(A, ia + e, ga + e, oa + e);
-      const int64_t mb = n - eb < 4 ? n - eb : 4;
-      for (int64_t e = 0; e < mb; ++e) step_at<GT>(A, ib + e, gb + e, ob + e);
+      const int64_t ip[2] = {ia, ib}, gp[2] = {ga, gb}, op[2] = {oa, ob};
+      const int cnt[2] = {(int)(n - ea < 4 ? n - ea : 4),
+                          (int)(n - eb <= 0 ? 0 : (n - eb < 4 ? n - eb : 4))};
+      step_upto8<ND, GT>(A, ip, gp, op, cnt);
     }
   }
 }
@@ -772,16 +823,23 @@ int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int3
     for (int64_t b = b0; b < b1; ++b)
       if ((L->bucket_slice(b) + span_e - 1) / span_e >= kMaxTableTiles) return ZERO_ERANGE;
     const int tcap = table_cap(nd, c.gt);
-    // table launches fill the chip better with two blocks per CU: each
-    // block does one chunk per wave between region look-ups (GPT-2, 148
-    // tensors: 0.137 ms with one block per CU, 0.123 ms with two)
-    const int tblocks = ls.blocks_cap > 0 ? ls.blocks_cap : cu_count() * 2;
+    // blocks of a table launch, measured with 256 threads on tuned pools:
+    // a launch of up to 64 tiles per CU is latency-bound (each block does one
+    // chunk per wave between region look-ups) and runs fastest with 16
+    // blocks per CU (GPT-2, 148 tensors, 7.6K tiles: 0.111 ms against 0.121
+    // with two and 0.133 with one); larger launches are bandwidth-bound and
+    // run fastest with one block per CU, as the vector kernel does (one
+    // Llama-3-8B layer, 13K tiles: equal; four layers: 0.737 ms against 0.763
+    // with two; the whole model: 6.70 ms against 7.13)
+    const int cus = cu_count();
     HostTable T;
     T.count = 0;
     T.vec_ok = allow_vec ? 1 : 0;
     auto flush = [&]() -> int {
       if (T.count == 0) return ZERO_OK;
       const int64_t total = T.tile0[T.count];
+      const int64_t tblocks =
+          ls.blocks_cap > 0 ? ls.blocks_cap : (int64_t)cus * (total <= (int64_t)64 * cus ? 16 : 1);
       const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(total, tblocks));
       const Work w{nullptr, &T, blocks, threads};
       const int rc = dispatch<K_TABLE>(c, w, stream);
