@@ -88,8 +88,9 @@ class Inputs:
 
 TUNE_SLACK = 32 << 30   # extra pool bytes over which the tuned placement may shift
 # the main workload's pool: (spare bytes, shift step) tried in order until one
-# fits; within a pool of 200+ GiB the fastest starts lie further in (llama8b:
-# 6.67 ms at 88 GiB against 6.73 ms within the first 32 GiB)
+# fits; the step's speed repeats with the arrangement's start with a period of
+# about 96 GiB whose phase differs between boxes, so the first choice searches
+# more than one period
 MAIN_TUNE = ((128 << 30, 8 << 30), (64 << 30, 8 << 30), (32 << 30, 4 << 30))
 
 
