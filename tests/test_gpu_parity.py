@@ -247,9 +247,9 @@ EDGE = [
 ]
 
 
-def _edge_case(numel, cap, n_d, rank, gl, om, t=3):
+def _edge_case(numel, cap, n_d, rank, gl, om, t=3, rows=None):
     w = workloads.Workload("edge", numel, cap, n_d, rank, gl, om, t, 1, ("normal", 1e-3),
-                           ("normal", 0.02), ("normal", 1e-4), ("absnormal", 1e-6))
+                           ("normal", 0.02), ("normal", 1e-4), ("absnormal", 1e-6), rows=rows)
     w.name = "flat1m"  # reuse a workload id for the generator keys
     return Case(w)
 
@@ -1309,6 +1309,52 @@ def test_dim0_launch_shape_invariance(launch):
         outs.append([case.master.cpu().numpy(), u16(case.pout), case.gout.cpu().numpy()])
     for a, b in zip(*outs):
         assert_bitwise(a, b, f"dim0 launch {launch}")
+
+
+DIM0_DTYPE_CASES = [
+    # shapes, n_d, rank, grad_layout, out_mode
+    ([(5, 3), (7,), (1, 9), (16, 16), (33, 17), (300, 40)], 4, 3, "flat", "ag_slot"),
+    ([(129, 64), (1000,), (2, 3), (64 * 40, 48)], 64, 5, "flat", "ag_slot"),
+    ([(100, 24), (3, 8), (64, 64), (1000, 24)], 8, 7, "compact", "ag_slot"),
+]
+
+
+@pytest.mark.parametrize("contrib", ["f32", "fused_bf16", "fused_f32"])
+@pytest.mark.parametrize("shapes,n_d,rank,gl,om", DIM0_DTYPE_CASES)
+def test_dim0_f32_and_fused_steps_full_compare(shapes, n_d, rank, gl, om, contrib):
+    """Per-parameter layouts with slot output run as table launches; fp32
+    contributions and the fused last micro-batch (bf16 or fp32) through them,
+    every element against the oracle, three steps.  Slices that end inside
+    a chunk take the table kernel's element-wise path."""
+    numel = [int(np.prod(sh)) for sh in shapes]
+    case = _edge_case(numel, 0, n_d, rank, gl, om, rows=[sh[0] for sh in shapes])
+    say(f"  dim0 {contrib} shapes={shapes} n_d={n_d} r={rank} {gl} {om}: S={case.S}")
+    case.init_state_gpu()
+    case.init_state_oracle()
+    flat = gl == "flat"
+    for t in (1, 2, 3):
+        if contrib == "f32":
+            dev, host = _f32_contribs(case, t, flat)
+            case.step_gpu(t, dev)
+            case.o_p, case.o_g = oracle.shard_step_f32(host, case.o_master, case.o_m, case.o_v,
+                                                       case.hp_o, t, want_grad=True)
+        else:
+            dt = z.DTYPE_BF16 if contrib == "fused_bf16" else z.DTYPE_F32
+            acc, o_acc = _contribs(case, t, flat, "grad", 0, ("normal", 1e-3), synth.OUT_F32)
+            mic, o_mic = _contribs(case, t, flat, "micro_grad", 3, ("normal", 2e-3),
+                                   synth.OUT_BF16)
+            z.zero_shard_step_accumulate(
+                case.L, case.hp_z, t, acc, mic, 0.25, dt,
+                z.GRAD_FLAT if flat else z.GRAD_COMPACT, case.master, case.m, case.v,
+                case.pout, z.OUT_AG_SLOT if om == "ag_slot" else z.OUT_SHARD, case.gout)
+            _fused_oracle(case, t, o_acc, o_mic, 0.25, dt)
+    torch.cuda.synchronize()
+    case.compare(f"dim0 {contrib}")
+    for a, b in ((case.master, case.o_master), (case.m, case.o_m), (case.v, case.o_v)):
+        assert_bitwise(a.cpu().numpy(), b, "state")
+    pos = case.flat_pos if om == "ag_slot" else np.arange(case.S)
+    assert_bitwise(u16(case.pout)[pos], case.o_p, "param")
+    case.check_canaries(n_probe=4096)
 
 
 @pytest.mark.timeout(600)
