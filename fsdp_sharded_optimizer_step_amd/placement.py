@@ -14,6 +14,11 @@ LANE_BYTES = 32 * GiB   # MI355X, measured: lanes 32 GiB apart ...
 N_LANES = 3             # ... three of them (a 96 GiB period)
 ALIGN = 2 << 20
 SLACK = 32 * GiB        # spare room measured to avoid the slow placements
+# (spare bytes, shift step) tried in order by tuned_step_pool until a pool
+# fits: the step's speed repeats with the arrangement's start with a period of
+# about 96 GiB whose phase differs between devices, so the first search
+# covers more than one period
+SEARCH = ((128 * GiB, 8 * GiB), (64 * GiB, 8 * GiB), (SLACK, 4 * GiB))
 
 
 class Pool:
@@ -123,9 +128,25 @@ def step_timer(layout, hp, t: int, grad_layout: int, out_mode: int, reps: int = 
 
 
 def tuned_step_pool(layout, hp, t: int, grad_layout: int = 0, out_mode: int = OUT_AG_SLOT,
-                    slack=SLACK, device="cuda:0", **spec_kw) -> Pool:
-    """step_pool with `slack` spare bytes, its start chosen by timing the
-    step at 4 GiB shifts (the buffers' contents are arbitrary afterwards)."""
-    return step_pool(layout, device=device, slack=slack, grad_layout=grad_layout,
-                     out_mode=out_mode,
-                     choose=step_timer(layout, hp, t, grad_layout, out_mode), **spec_kw)
+                    slack=None, device="cuda:0", **spec_kw) -> Pool:
+    """step_pool with spare bytes, its start chosen by timing the step at
+    shifts over the spare room (the buffers' contents are arbitrary
+    afterwards).  slack=None tries the (spare bytes, shift step) pairs of
+    SEARCH in order until a pool fits on the device; an explicit `slack`
+    (with `shift_step`, default 4 GiB) makes one attempt."""
+    import torch
+    choose = step_timer(layout, hp, t, grad_layout, out_mode)
+    if slack is not None:
+        return step_pool(layout, device=device, slack=slack, grad_layout=grad_layout,
+                         out_mode=out_mode, choose=choose, **spec_kw)
+    if "shift_step" in spec_kw:
+        raise TypeError("tuned_step_pool: shift_step needs an explicit slack")
+    last = None
+    for sl, step in SEARCH:
+        try:
+            return step_pool(layout, device=device, slack=sl, grad_layout=grad_layout,
+                             out_mode=out_mode, choose=choose, shift_step=step, **spec_kw)
+        except torch.cuda.OutOfMemoryError as e:
+            last = e
+            torch.cuda.empty_cache()
+    raise last

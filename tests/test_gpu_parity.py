@@ -318,6 +318,20 @@ def test_tuned_step_pool_times_the_step_at_each_shift():
     assert len(pool.grads) == 8 and pool["param_out"].numel() == L.shard
 
 
+def test_tuned_step_pool_falls_back_to_a_search_that_fits(monkeypatch):
+    """With no explicit slack the helper tries its searches in order: one
+    whose pool cannot be allocated is skipped for the next."""
+    from fsdp_sharded_optimizer_step_amd import placement as zp
+    monkeypatch.setattr(zp, "SEARCH", ((1 << 50, 1 << 20), (2 << 20, 1 << 20)))
+    L = z.Layout([300_001, 77], 65_536, 8, 5)
+    pool = zp.tuned_step_pool(L, z.AdamW(), 1, z.GRAD_COMPACT, z.OUT_SHARD,
+                              lane_bytes=1 << 20, align=256)
+    assert [sh for sh, _ in pool.tuning] == [0, 1 << 20, 2 << 20]
+    assert pool.shift == min(pool.tuning, key=lambda x: x[1])[0]
+    with pytest.raises(TypeError):
+        zp.tuned_step_pool(L, z.AdamW(), 1, shift_step=1 << 20)
+
+
 def test_empty_shard_is_a_no_op():
     L = z.Layout([], 0, 4, 0)
     e = torch.empty(0, dtype=torch.float32, device=DEV)
