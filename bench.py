@@ -87,11 +87,9 @@ class Inputs:
 
 
 TUNE_SLACK = 32 << 30   # extra pool bytes over which the tuned placement may shift
-# the main workload's pool: (spare bytes, shift step) tried in order until one
-# fits; the step's speed repeats with the arrangement's start with a period of
-# about 96 GiB whose phase differs between boxes, so the first choice searches
-# more than one period
-MAIN_TUNE = ((128 << 30, 8 << 30), (64 << 30, 8 << 30), (32 << 30, 4 << 30))
+# the main workload's pool: the library helper's search, (spare bytes, shift
+# step) pairs tried in order until a pool fits
+from fsdp_sharded_optimizer_step_amd.placement import SEARCH as MAIN_TUNE  # noqa: E402
 
 
 def step_call(z, L, hp, t, grad_layout, out_mode, fused=False):
