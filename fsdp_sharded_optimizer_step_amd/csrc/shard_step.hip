@@ -838,8 +838,12 @@ int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int3
     auto flush = [&]() -> int {
       if (T.count == 0) return ZERO_OK;
       const int64_t total = T.tile0[T.count];
+      // in waves per CU: 64 for small launches, 4 for large ones (one
+      // 256-thread block, or two 128-thread blocks for fp32 contributions)
+      const int64_t waves_per_cu = total <= (int64_t)64 * cus ? 64 : 4;
       const int64_t tblocks =
-          ls.blocks_cap > 0 ? ls.blocks_cap : (int64_t)cus * (total <= (int64_t)64 * cus ? 16 : 1);
+          ls.blocks_cap > 0 ? ls.blocks_cap
+                            : (int64_t)cus * std::max<int64_t>(1, waves_per_cu / (threads / 64));
       const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(total, tblocks));
       const Work w{nullptr, &T, blocks, threads};
       const int rc = dispatch<K_TABLE>(c, w, stream);
