@@ -558,6 +558,97 @@ def all_configs(z, synth, workloads, steps, warmup, placement):
     return res
 
 
+def time_steps(z, w, L, inp, steps, warmup, stream, launch=None):
+    """Warmup, then `steps` timed calls of zero_shard_step on resident inputs
+    (t advancing), each bracketed by HIP events on the launch stream; the
+    whole timed region is also measured on the host clock, synchronised on
+    both sides.  -> (host ms per step, per-call kernel ms list, next t)."""
+    import torch
+    hp = z.AdamW(**w.hp)
+    gl = z.GRAD_COMPACT if w.grad_layout == "compact" else z.GRAD_FLAT
+    om = z.OUT_AG_SLOT if w.out_mode == "ag_slot" else z.OUT_SHARD
+
+    def step(t):
+        z.zero_shard_step(L, hp, t, inp.grads, gl, *inp.state, inp.pout, om, launch=launch,
+                          stream=stream)
+
+    t = w.t_first
+    for _ in range(warmup):
+        step(t)
+        t += 1
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev[k][0].record(stream)
+        step(t)
+        ev[k][1].record(stream)
+        t += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, [a.elapsed_time(b) for a, b in ev], t
+
+
+def roofline_block(w, S, kernel_ms):
+    """The step kernel's algorithmic bytes per launch over its average
+    launch duration, against 8 TB/s; traffic from the committed counter
+    summary when it was taken on the current kernel sources."""
+    k_avg = sum(kernel_ms) / len(kernel_ms)
+    alg_bytes = S * (2 * w.n_d + 26)
+    achieved = alg_bytes / (k_avg * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic_from_profiles(w.name, alg_bytes),
+            "kernel": step_kernel_name(w.n_d, w.grad_layout == "flat" or w.out_mode == "ag_slot"),
+            "kernel_avg_ms": k_avg, "kernel_median_ms": sorted(kernel_ms)[len(kernel_ms) // 2],
+            "kernel_min_ms": min(kernel_ms), "algorithmic_bytes_per_launch": alg_bytes,
+            "kernel_hash": kernel_hash()}
+
+
+def placement_info(inp):
+    if inp.pool is None:
+        return "separate", None
+    return "tuned", {"pool_GiB": inp.pool.nbytes / 2**30,
+                     "chosen_shift_GiB": inp.pool.shift / 2**30,
+                     "ms_by_shift_GiB": [[sh / 2**30, ms] for sh, ms in inp.pool.tuning]}
+
+
+def second_config(z, synth, name, args, stream):
+    """One more full-size workload in the same run (its own buffers, freed
+    afterwards): step time, roofline block and CPU oracle."""
+    import torch
+    w = workloads_mod().get(name)
+    L = z.Layout(w.numel, w.cap, w.n_d, w.rank)
+    S, P = L.shard, L.padded
+    print(f"# workload {w.name}: S={S} P={P} N_d={w.n_d} buckets={L.n_buckets}", file=sys.stderr,
+          flush=True)
+    inp, segs = make_inputs(z, synth, w, L, args.placement, tune=MAIN_TUNE)
+    used, tuning = placement_info(inp)
+    ms_per_step, kernel_ms, _ = time_steps(z, w, L, inp, args.steps, args.warmup, stream)
+    roof = roofline_block(w, S, kernel_ms)
+    print(f"# {w.name}: {ms_per_step:.3f} ms/step wall, kernel avg {roof['kernel_avg_ms']:.3f} ms; "
+          f"{roof['achieved']:.0f} GB/s ({100 * roof['frac']:.1f} % of 8 TB/s)", file=sys.stderr,
+          flush=True)
+    del inp
+    torch.cuda.empty_cache()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, segs, S, target_s=8.0)
+    bpe = 2 * w.n_d + 26
+    return {"workload": w.name, "description": WORKLOAD_LABEL[w.name], "shard_elems": S,
+            "padded_elems": P, "n_d": w.n_d, "rank": w.rank, "buckets": L.n_buckets,
+            "grad_layout": w.grad_layout, "out_mode": w.out_mode, "bytes_per_elem": bpe,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+            "value": S / (ms_per_step * 1e-3), "unit": "elem/s",
+            "hbm_GBps": S * bpe / (ms_per_step * 1e-3) / 1e9,
+            "hbm_frac_of_peak": S * bpe / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "placement": used, "placement_tuning": tuning, "roofline": roof, "cpu_baseline": cpu}
+
+
+def workloads_mod():
+    from synth import workloads
+    return workloads
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -566,6 +657,9 @@ def main():
     ap.add_argument("--workload", default="llama8b", choices=sorted(WORKLOAD_LABEL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-aux", action="store_true", help="skip the pack/accumulate timings")
+    ap.add_argument("--no-more-configs", action="store_true",
+                    help="time only --workload (by default the Llama-3-8B run also times the "
+                         "two Llama-70B shards, N_d = 64, in the same JSON line)")
     ap.add_argument("--blocks", type=int, default=0)
     ap.add_argument("--threads", type=int, default=0)
     ap.add_argument("--placement", default="tuned", choices=["tuned", "planned", "separate"],
@@ -610,41 +704,19 @@ def main():
     print(f"# workload {w.name}: S={S} P={P} N_d={w.n_d} buckets={L.n_buckets}", file=sys.stderr,
           flush=True)
     inp, segs = make_inputs(z, synth, w, L, args.placement, tune=MAIN_TUNE)
-    placement_used = "separate" if inp.pool is None else args.placement
+    placement_used, tuning = placement_info(inp)
+    if placement_used == "tuned" and args.placement != "tuned":
+        placement_used = args.placement
     hp = z.AdamW(**w.hp)
     gl = z.GRAD_COMPACT if w.grad_layout == "compact" else z.GRAD_FLAT
     om = z.OUT_AG_SLOT if w.out_mode == "ag_slot" else z.OUT_SHARD
     launch = (args.blocks, args.threads, 0) if (args.blocks or args.threads) else None
     stream = torch.cuda.current_stream()
-
-    def step(t):
-        z.zero_shard_step(L, hp, t, inp.grads, gl, *inp.state, inp.pout, om, launch=launch,
-                          stream=stream)
-
-    t = w.t_first
-    for _ in range(args.warmup):
-        step(t)
-        t += 1
-    torch.cuda.synchronize()
-    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        step(t)
-        ev[k][1].record(stream)
-        t += 1
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = [a.elapsed_time(b) for a, b in ev]
-    ms_per_step = wall * 1e3 / args.steps
-    k_avg = sum(kernel_ms) / len(kernel_ms)
+    ms_per_step, kernel_ms, t = time_steps(z, w, L, inp, args.steps, args.warmup, stream, launch)
+    roof = roofline_block(w, S, kernel_ms)
+    k_avg, achieved, alg_bytes = roof["kernel_avg_ms"], roof["achieved"], roof[
+        "algorithmic_bytes_per_launch"]
     bytes_per_elem = 2 * w.n_d + 26
-    alg_bytes = S * bytes_per_elem
-    achieved = alg_bytes / (k_avg * 1e-3) / 1e9
-    traffic = traffic_from_profiles(w.name, alg_bytes)
     print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, kernel avg {k_avg:.3f} ms "
           f"(min {min(kernel_ms):.3f}, max {max(kernel_ms):.3f}); {achieved:.0f} GB/s",
           file=sys.stderr, flush=True)
@@ -658,30 +730,29 @@ def main():
     print(f"# pure read {probes['read']['GBps']:.0f} GB/s, copy {probes['copy']['GBps']:.0f} GB/s "
           "on the same buffers", file=sys.stderr, flush=True)
     nxt = []
-    tuning = None
-    if inp.pool is not None:
-        tuning = {"pool_GiB": inp.pool.nbytes / 2**30, "chosen_shift_GiB": inp.pool.shift / 2**30,
-                  "ms_by_shift_GiB": [[sh / 2**30, ms] for sh, ms in inp.pool.tuning]}
     holder = [inp]
     del inp
     if not args.no_aux and w.name == "llama8b":
         nxt = next_rows(z, synth, w, L, holder, make_timer(stream), args.placement)
     holder.clear()
     torch.cuda.empty_cache()
-    # the same step on one torch allocation per buffer, for comparison
-    other = None
+    # the same step on placements that need no timed search: one torch
+    # allocation per buffer, and the planned pool at its start
+    other = {}
     if not args.no_aux:
-        alt = "separate" if placement_used != "separate" else "tuned"
-        inp, _ = make_inputs(z, synth, w, L, alt)
-        ms_alt = make_timer(stream)(lambda: z.zero_shard_step(L, hp, t, inp.grads, gl, *inp.state,
-                                                              inp.pout, om), reps=10)
-        other = {"placement": alt, "kernel_avg_ms": ms_alt,
-                 "GBps": alg_bytes / (ms_alt * 1e-3) / 1e9,
-                 "frac": alg_bytes / (ms_alt * 1e-3) / 1e9 / PEAK_HBM_GBPS}
-        print(f"# placement {alt}: {ms_alt:.3f} ms, {other['GBps']:.0f} GB/s", file=sys.stderr,
-              flush=True)
-        del inp
-    torch.cuda.empty_cache()
+        for alt in ("separate", "planned"):
+            inp, _ = make_inputs(z, synth, w, L, alt)
+            ms_alt = make_timer(stream)(lambda: z.zero_shard_step(
+                L, hp, t, inp.grads, gl, *inp.state, inp.pout, om), reps=10)
+            work = sum(x.numel() * x.element_size() for x in inp.grads + inp.state + [inp.pout])
+            other[alt] = {"kernel_avg_ms": ms_alt, "GBps": alg_bytes / (ms_alt * 1e-3) / 1e9,
+                          "frac": alg_bytes / (ms_alt * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                          "buffer_GiB": work / 2**30,
+                          "pool_GiB": None if inp.pool is None else inp.pool.nbytes / 2**30}
+            print(f"# placement {alt}: {ms_alt:.3f} ms, {other[alt]['GBps']:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+            del inp
+            torch.cuda.empty_cache()
     aux = nxt + ([] if args.no_aux else aux_kernels(z, synth, workloads, args.placement))
     for a in aux:
         print(f"# {a.get('row', a['kernel'])}: {a['ms']:.3f} ms, {a['GBps']:.0f} GB/s "
@@ -689,6 +760,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, segs, S)
+    more = {}
+    if w.name == "llama8b" and not args.no_more_configs:
+        for name in ("llama70b", "llama70b_t"):
+            more[name] = second_config(z, synth, name, args, stream)
     out = {
         "metric": "shard-step elements/s and achieved HBM GB/s (% of MI355X peak), 1 GPU",
         "value": S / (ms_per_step * 1e-3),
@@ -709,15 +784,9 @@ def main():
                    "grad_layout": w.grad_layout, "out_mode": w.out_mode,
                    "bytes_per_elem": bytes_per_elem, "io": "bf16 grads and params, f32 state",
                    "placement": placement_used, "placement_tuning": tuning},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "kernel": step_kernel_name(w.n_d, w.grad_layout == "flat"
-                                                or w.out_mode == "ag_slot"),
-                     "kernel_avg_ms": k_avg,
-                     "kernel_median_ms": sorted(kernel_ms)[len(kernel_ms) // 2],
-                     "kernel_min_ms": min(kernel_ms),
-                     "algorithmic_bytes_per_launch": alg_bytes, "kernel_hash": kernel_hash()},
+        "roofline": roof,
         "cpu_baseline": cpu,
+        "configs": more,
         "same_mix_ceiling": {"GBps": ceil_gbps, "frac_of_peak": ceil_gbps / PEAK_HBM_GBPS,
                              "step_frac_of_ceiling": achieved / ceil_gbps,
                              "kernel": "measure/stream_ceiling.hip: the step's bytes, "

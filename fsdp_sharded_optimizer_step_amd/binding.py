@@ -27,7 +27,8 @@ EXPORTS = ("zero_layout_create", "zero_layout_destroy", "zero_layout_psi", "zero
            "zero_layout_bucket", "zero_layout_tensor", "zero_bucket_pack", "zero_grad_accumulate",
            "zero_shard_step", "zero_shard_step_ex", "zero_step_scalars", "zero_strerror",
            "zero_gather_params", "zero_reshard", "zero_layout_create_dim0", "zero_layout_kind",
-           "zero_shard_step_accumulate", "zero_placement_plan", "zero_shard_step_buckets")
+           "zero_shard_step_accumulate", "zero_placement_plan", "zero_shard_step_buckets",
+           "zero_layout_tensor_flat")
 
 
 class ZeroError(RuntimeError):
@@ -80,6 +81,7 @@ def load():
         getattr(lib, name).restype = C.c_int32
     lib.zero_layout_bucket.argtypes = [vp, C.c_int64] + [_i64p] * 5
     lib.zero_layout_tensor.argtypes = [vp, C.c_int32] + [_i64p] * 3
+    lib.zero_layout_tensor_flat.argtypes = [vp, C.c_int32] + [_i64p] * 2
     lib.zero_bucket_pack.argtypes = [vp, C.POINTER(vp), C.c_int64, C.c_int64, vp, vp]
     lib.zero_grad_accumulate.argtypes = [vp, vp, C.c_int64, C.c_float, C.c_uint32, vp, vp]
     lib.zero_shard_step.argtypes = [vp, C.POINTER(_AdamW), C.c_int64, C.POINTER(vp), C.c_int32,
@@ -147,6 +149,7 @@ class Layout:
                 arr, rarr, len(numel), int(n_d), int(rank), C.byref(h)))
         self._h = h
         self.n_tensors = len(numel)
+        self.numel = [int(n) for n in numel]
 
     @property
     def handle(self):
@@ -181,6 +184,13 @@ class Layout:
         _check("zero_layout_tensor", load().zero_layout_tensor(self._h, t, *[C.byref(v) for v in vals]))
         return tuple(v.value for v in vals)
 
+    def tensor_flat(self, t: int):
+        """-> (flat_lo, flat_hi): tensor t's range in the padded flat buffer"""
+        vals = [C.c_int64() for _ in range(2)]
+        _check("zero_layout_tensor_flat",
+               load().zero_layout_tensor_flat(self._h, t, *[C.byref(v) for v in vals]))
+        return tuple(v.value for v in vals)
+
 
 def _stream_ptr(stream):
     import torch
@@ -188,29 +198,61 @@ def _stream_ptr(stream):
     return C.c_void_p(s.cuda_stream)
 
 
-def _dev16(t, name):
+def _need(t, name, n):
+    """The C ABI receives bare pointers and cannot know buffer lengths: a
+    tensor shorter than what the call reads or writes would become an
+    out-of-bounds device access, so it is refused here (before the dtype and
+    device checks, so the check also runs on a host without a GPU)."""
+    if t is not None and n is not None and t.numel() < n:
+        raise ValueError(f"{name}: has {t.numel()} elements, the call needs at least {n}")
+
+
+def _dev16(t, name, n=None):
     if t is None:
         return None
+    _need(t, name, n)
     if not (t.is_cuda and t.is_contiguous() and t.element_size() == 2):
         raise ValueError(f"{name}: needs a contiguous 16-bit CUDA tensor")
     return C.c_void_p(t.data_ptr())
 
 
-def _dev32(t, name):
+def _dev32(t, name, n=None):
     import torch
     if t is None:
         return None
+    _need(t, name, n)
     if not (t.is_cuda and t.is_contiguous() and t.dtype == torch.float32):
         raise ValueError(f"{name}: needs a contiguous float32 CUDA tensor")
     return C.c_void_p(t.data_ptr())
 
 
-def _ptr_array(tensors, name, check=None):
+def _ptr_array(tensors, name, check=None, n=None):
+    """Host array of device pointers; `n`: the elements each entry must hold
+    (an int for all, or a list with one entry per tensor)."""
     check = check or _dev16
     arr = (C.c_void_p * max(1, len(tensors)))()
     for k, t in enumerate(tensors):
-        arr[k] = None if t is None else check(t, f"{name}[{k}]").value
+        nk = n[k] if isinstance(n, (list, tuple)) else n
+        arr[k] = None if t is None else check(t, f"{name}[{k}]", nk).value
     return arr
+
+
+def _sizes(*items):
+    """(tensor or list of tensors, name, elements needed) for every buffer
+    of a call, checked before any pointer is marshalled."""
+    for ts, name, n in items:
+        if isinstance(ts, (list, tuple)):
+            for k, t in enumerate(ts):
+                _need(t, f"{name}[{k}]", n[k] if isinstance(n, (list, tuple)) else n)
+        else:
+            _need(ts, name, n)
+
+
+def _step_sizes(layout: Layout, grad_layout: int, out_mode: int):
+    """(elements per contribution, per state array, of the parameter output)
+    of a step call on `layout`."""
+    S, P = layout.shard, layout.padded
+    return (P if grad_layout == GRAD_FLAT else S), S, (P if out_mode == OUT_AG_SLOT else S)
 
 
 def zero_bucket_pack(layout: Layout, tensor_grads, flat_out, bucket_begin: int = 0,
@@ -218,17 +260,19 @@ def zero_bucket_pack(layout: Layout, tensor_grads, flat_out, bucket_begin: int =
     if len(tensor_grads) != layout.n_tensors:
         raise ValueError("zero_bucket_pack: one pointer per tensor is required")
     end = layout.n_buckets if bucket_end is None else bucket_end
+    _sizes((tensor_grads, "tensor_grads", layout.numel), (flat_out, "flat_out", layout.padded))
     _check("zero_bucket_pack", load().zero_bucket_pack(
-        layout.handle, _ptr_array(tensor_grads, "tensor_grads"), bucket_begin, end,
-        _dev16(flat_out, "flat_out"), _stream_ptr(stream)))
+        layout.handle, _ptr_array(tensor_grads, "tensor_grads", n=layout.numel), bucket_begin,
+        end, _dev16(flat_out, "flat_out", layout.padded), _stream_ptr(stream)))
 
 
 def zero_grad_accumulate(acc, grad, scale: float, flags: int = 0, bf16_out=None, n=None,
                          stream=None):
-    n = grad.numel() if n is None else n
+    n = grad.numel() if n is None else int(n)
+    _sizes((acc, "acc", n), (grad, "grad", n), (bf16_out, "bf16_out", n))
     _check("zero_grad_accumulate", load().zero_grad_accumulate(
-        _dev32(acc, "acc"), _dev16(grad, "grad"), n, scale, flags, _dev16(bf16_out, "bf16_out"),
-        _stream_ptr(stream)))
+        _dev32(acc, "acc", n), _dev16(grad, "grad", n), n, scale, flags,
+        _dev16(bf16_out, "bf16_out", n), _stream_ptr(stream)))
 
 
 def zero_shard_step(layout: Layout, hp: AdamW, t: int, rank_grads, grad_layout: int, master,
@@ -241,11 +285,15 @@ def zero_shard_step(layout: Layout, hp: AdamW, t: int, rank_grads, grad_layout: 
     if len(rank_grads) != layout.n_d:
         raise ValueError("zero_shard_step: one contribution per rank is required")
     f32 = len(rank_grads) > 0 and rank_grads[0] is not None and rank_grads[0].dtype == torch.float32
-    grads = _ptr_array(rank_grads, "rank_grads", _dev32 if f32 else _dev16)
+    ng, ns, no = _step_sizes(layout, grad_layout, out_mode)
+    _sizes((rank_grads, "rank_grads", ng), (master, "master", ns), (exp_avg, "exp_avg", ns),
+           (exp_avg_sq, "exp_avg_sq", ns), (param_out, "param_out", no),
+           (reduced_grad_out, "reduced_grad_out", ns))
+    grads = _ptr_array(rank_grads, "rank_grads", _dev32 if f32 else _dev16, ng)
     args = [layout.handle, C.byref(hp._c()), int(t), grads, grad_layout,
-            _dev32(master, "master"), _dev32(exp_avg, "exp_avg"),
-            _dev32(exp_avg_sq, "exp_avg_sq"), _dev16(param_out, "param_out"), out_mode,
-            _dev32(reduced_grad_out, "reduced_grad_out")]
+            _dev32(master, "master", ns), _dev32(exp_avg, "exp_avg", ns),
+            _dev32(exp_avg_sq, "exp_avg_sq", ns), _dev16(param_out, "param_out", no), out_mode,
+            _dev32(reduced_grad_out, "reduced_grad_out", ns)]
     if launch is None and not f32:
         _check("zero_shard_step", load().zero_shard_step(*args, _stream_ptr(stream)))
     else:
@@ -267,12 +315,16 @@ def zero_shard_step_buckets(layout: Layout, hp: AdamW, t: int, bucket_begin: int
     f32 = len(rank_grads) > 0 and rank_grads[0] is not None and rank_grads[0].dtype == torch.float32
     blocks, threads, path = launch if launch is not None else (0, 0, 0)
     opt = _Options(DTYPE_F32 if f32 else DTYPE_BF16, blocks, threads, path)
+    ng, ns, no = _step_sizes(layout, grad_layout, out_mode)
+    _sizes((rank_grads, "rank_grads", ng), (master, "master", ns), (exp_avg, "exp_avg", ns),
+           (exp_avg_sq, "exp_avg_sq", ns), (param_out, "param_out", no),
+           (reduced_grad_out, "reduced_grad_out", ns))
     _check("zero_shard_step_buckets", load().zero_shard_step_buckets(
         layout.handle, C.byref(hp._c()), int(t), int(bucket_begin), int(bucket_end),
-        _ptr_array(rank_grads, "rank_grads", _dev32 if f32 else _dev16), grad_layout,
-        _dev32(master, "master"), _dev32(exp_avg, "exp_avg"), _dev32(exp_avg_sq, "exp_avg_sq"),
-        _dev16(param_out, "param_out"), out_mode, _dev32(reduced_grad_out, "reduced_grad_out"),
-        C.byref(opt), _stream_ptr(stream)))
+        _ptr_array(rank_grads, "rank_grads", _dev32 if f32 else _dev16, ng), grad_layout,
+        _dev32(master, "master", ns), _dev32(exp_avg, "exp_avg", ns),
+        _dev32(exp_avg_sq, "exp_avg_sq", ns), _dev16(param_out, "param_out", no), out_mode,
+        _dev32(reduced_grad_out, "reduced_grad_out", ns), C.byref(opt), _stream_ptr(stream)))
 
 
 def zero_shard_step_accumulate(layout: Layout, hp: AdamW, t: int, rank_acc, rank_micro,
@@ -286,12 +338,16 @@ def zero_shard_step_accumulate(layout: Layout, hp: AdamW, t: int, rank_acc, rank
                          "gradient per rank are required")
     blocks, threads, path = launch if launch is not None else (0, 0, 0)
     opt = _Options(contrib_dtype, blocks, threads, path)
+    ng, ns, no = _step_sizes(layout, grad_layout, out_mode)
+    _sizes((rank_acc, "rank_acc", ng), (rank_micro, "rank_micro", ng), (master, "master", ns),
+           (exp_avg, "exp_avg", ns), (exp_avg_sq, "exp_avg_sq", ns),
+           (param_out, "param_out", no), (reduced_grad_out, "reduced_grad_out", ns))
     _check("zero_shard_step_accumulate", load().zero_shard_step_accumulate(
-        layout.handle, C.byref(hp._c()), int(t), _ptr_array(rank_acc, "rank_acc", _dev32),
-        _ptr_array(rank_micro, "rank_micro"), float(micro_scale), contrib_dtype, grad_layout,
-        _dev32(master, "master"), _dev32(exp_avg, "exp_avg"), _dev32(exp_avg_sq, "exp_avg_sq"),
-        _dev16(param_out, "param_out"), out_mode, _dev32(reduced_grad_out, "reduced_grad_out"),
-        C.byref(opt), _stream_ptr(stream)))
+        layout.handle, C.byref(hp._c()), int(t), _ptr_array(rank_acc, "rank_acc", _dev32, ng),
+        _ptr_array(rank_micro, "rank_micro", n=ng), float(micro_scale), contrib_dtype,
+        grad_layout, _dev32(master, "master", ns), _dev32(exp_avg, "exp_avg", ns),
+        _dev32(exp_avg_sq, "exp_avg_sq", ns), _dev16(param_out, "param_out", no), out_mode,
+        _dev32(reduced_grad_out, "reduced_grad_out", ns), C.byref(opt), _stream_ptr(stream)))
 
 
 def zero_gather_params(layout: Layout, rank_shards, full_out, bucket_begin: int = 0,
@@ -299,9 +355,10 @@ def zero_gather_params(layout: Layout, rank_shards, full_out, bucket_begin: int 
     if len(rank_shards) != layout.n_d:
         raise ValueError("zero_gather_params: one shard per rank is required")
     end = layout.n_buckets if bucket_end is None else bucket_end
+    _sizes((rank_shards, "rank_shards", layout.shard), (full_out, "full_out", layout.padded))
     _check("zero_gather_params", load().zero_gather_params(
-        layout.handle, _ptr_array(rank_shards, "rank_shards"), bucket_begin, end,
-        _dev16(full_out, "full_out"), _stream_ptr(stream)))
+        layout.handle, _ptr_array(rank_shards, "rank_shards", n=layout.shard), bucket_begin, end,
+        _dev16(full_out, "full_out", layout.padded), _stream_ptr(stream)))
 
 
 def zero_reshard(src: Layout, src_shards, dst: Layout, dst_shard, stream=None):
@@ -310,11 +367,12 @@ def zero_reshard(src: Layout, src_shards, dst: Layout, dst_shard, stream=None):
     import torch
     if len(src_shards) != src.n_d:
         raise ValueError("zero_reshard: one shard per source rank is required")
+    _sizes((src_shards, "src_shards", src.shard), (dst_shard, "dst_shard", dst.shard))
     f32 = dst_shard.dtype == torch.float32
     chk = _dev32 if f32 else _dev16
     _check("zero_reshard", load().zero_reshard(
-        src.handle, _ptr_array(src_shards, "src_shards", chk), dst.handle,
-        chk(dst_shard, "dst_shard"), 4 if f32 else 2, _stream_ptr(stream)))
+        src.handle, _ptr_array(src_shards, "src_shards", chk, src.shard), dst.handle,
+        chk(dst_shard, "dst_shard", dst.shard), 4 if f32 else 2, _stream_ptr(stream)))
 
 
 def zero_step_scalars(hp: AdamW, t: int):

@@ -53,4 +53,11 @@ __device__ __forceinline__ uint32_t bf16_pack2(float lo, float hi) {
   return bf16_round(lo) | (bf16_round(hi) << 16);
 }
 
+// Host side: a HIP error already pending on the calling thread, left by an
+// earlier unrelated call, would be read back by the launch check of an entry
+// point as if its own launch had failed, after part of its work was enqueued.
+// Entry points test for one before enqueuing anything and return ZERO_EHIP
+// without touching it, so the caller still reads it with hipGetLastError.
+inline bool hip_error_pending() { return hipPeekAtLastError() != hipSuccess; }
+
 }  // namespace zs

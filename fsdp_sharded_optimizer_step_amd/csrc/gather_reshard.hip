@@ -407,6 +407,7 @@ int zero_gather_params(const zero_layout* L, const uint16_t* const* rank_shards,
   // items over all runs <= P / tile + (number of buckets) * n_d
   if (L->P / kGatherTile + (bucket_end - bucket_begin) * (int64_t)nd >= (int64_t)0xffffffff)
     return ZERO_ERANGE;
+  if (hip_error_pending()) return ZERO_EHIP;
   if (L->fixed()) {
     const int64_t last = L->nb - 1;
     const int64_t full_end = std::min(bucket_end, last);
@@ -470,6 +471,7 @@ int zero_reshard(const zero_layout* src, const void* const* src_shards, const ze
       return ZERO_EOVERLAP;
   }
   if (dst->S == 0) return ZERO_OK;
+  if (hip_error_pending()) return ZERO_EHIP;
 
   // One `launch`: destination range [i0, i0+n) read through geometry gd
   // (origin d_base_i / d_base_x), source through gs with its pointers

@@ -164,6 +164,27 @@ int zero_layout_tensor(const zero_layout* L, int32_t t, int64_t* stream_off, int
   return ZERO_OK;
 }
 
+int zero_layout_tensor_flat(const zero_layout* L, int32_t t, int64_t* flat_lo, int64_t* flat_hi) {
+  if (!L) return ZERO_EINVAL;
+  if (t < 0 || t >= (int32_t)L->numel.size()) return ZERO_ERANGE;
+  const int64_t a = L->tensor_off[t], n = L->numel[t];
+  int64_t lo, hi;
+  if (!L->fixed()) {
+    // the tensor's real rows open its padded slot
+    lo = L->t_padded_off[t];
+    hi = lo + n;
+  } else {
+    // stream position x lies in bucket x / cap, at the same offset from the
+    // bucket's start in the padded flat buffer
+    auto flat = [&](int64_t x) { return (x / L->cap) * L->p_full + x % L->cap; };
+    lo = a < L->psi ? flat(a) : L->P;
+    hi = n > 0 ? flat(a + n - 1) + 1 : lo;
+  }
+  if (flat_lo) *flat_lo = lo;
+  if (flat_hi) *flat_hi = hi;
+  return ZERO_OK;
+}
+
 const char* zero_strerror(int status) {
   switch (status) {
     case ZERO_OK: return "ok";

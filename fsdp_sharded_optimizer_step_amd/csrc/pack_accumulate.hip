@@ -228,6 +228,8 @@ int zero_bucket_pack(const zero_layout* L, const uint16_t* const* tensor_grads,
       tiles += piece_tiles(pieces[k]);
     if (tiles > 0x7fffffff) return ZERO_ERANGE;
   }
+  if (pieces.empty()) return ZERO_OK;
+  if (hip_error_pending()) return ZERO_EHIP;
   for (size_t p0 = 0; p0 < pieces.size(); p0 += kPiecesPerLaunch) {
     PackArgs A;
     A.out = flat_out;
@@ -262,6 +264,7 @@ int zero_grad_accumulate(float* acc, const uint16_t* grad, int64_t n, float scal
   if (overlap(grad, 2 * n, acc, 4 * n) || (emit && (overlap(bf16_out, 2 * n, grad, 2 * n) ||
                                                    overlap(bf16_out, 2 * n, acc, 4 * n))))
     return ZERO_EOVERLAP;
+  if (hip_error_pending()) return ZERO_EHIP;
   // Launch policy, measured on MI355X for the three call kinds (blocks of
   // 256 threads per CU, cache policy).
   const int64_t cap = (int64_t)cus() * kAccBlocksPerCu;

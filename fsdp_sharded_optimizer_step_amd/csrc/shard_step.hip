@@ -800,6 +800,8 @@ int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int3
       if (overlaps(outs[a], span(ins[q], in_bytes[q]))) return ZERO_EOVERLAP;
   }
 
+  if (hip_error_pending()) return ZERO_EHIP;
+
   c.nd = nd;
   c.k = make_scalars(*hp, t);
   c.flat_grad = grad_layout == ZERO_GRAD_FLAT;

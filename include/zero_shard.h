@@ -34,7 +34,14 @@
  *   - Work is enqueued on `stream` (NULL = the null stream) and is
  *     asynchronous; results are visible after the caller synchronises.
  *     A failed launch returns ZERO_EHIP; faults during execution surface at
- *     the caller's next synchronisation.
+ *     the caller's next synchronisation.  A HIP error already pending on the
+ *     calling thread (hipPeekAtLastError) makes a call return ZERO_EHIP
+ *     before it enqueues anything, leaving that error for the caller to read.
+ *     A call that enqueues several kernels and sees one of its own launches
+ *     fail returns ZERO_EHIP with the earlier launches already enqueued: the
+ *     outputs (for a step: master, m, v and the parameters) may then be
+ *     partly updated, and repeating the call would apply the update twice to
+ *     that part; restore the state before retrying.
  *   - bf16 values are passed as their 16-bit patterns (uint16_t).
  *   - Arithmetic is binary32 with every operation rounded to nearest-even,
  *     no fused multiply-add, subnormals kept, correctly rounded division
@@ -143,6 +150,19 @@ int zero_layout_bucket(const zero_layout* layout, int64_t b, int64_t* stream_off
  * the end of a padded bucket.  Errors as for zero_layout_bucket. */
 int zero_layout_tensor(const zero_layout* layout, int32_t t, int64_t* stream_off,
                        int64_t* shard_lo, int64_t* shard_hi);
+
+/* Tensor t in the padded flat buffer (a rank's gradient bucket buffer, the
+ * All-Gather output): flat_lo is the flat offset of its first element and
+ * flat_hi one past that of its last, so a tensor that lies in one bucket
+ * occupies exactly [flat_lo, flat_hi); one that straddles buckets has the
+ * padding of every bucket it crosses inside that range ("FSDP1": the
+ * flattened parameters are concatenated and each bucket is padded at its
+ * end).  For the per-parameter layout the range opens the tensor's padded
+ * slot of n_d*c_t rows.  An empty tensor gets flat_lo == flat_hi, the
+ * position where it would start.  Null outputs are skipped.  Errors as for
+ * zero_layout_bucket. */
+int zero_layout_tensor_flat(const zero_layout* layout, int32_t t, int64_t* flat_lo,
+                            int64_t* flat_hi);
 
 /* ------------------------------------------------------------- bucket pack
  * ("Naive Data Parallelism": a bucket carries the gradients of several

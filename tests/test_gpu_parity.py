@@ -3,9 +3,8 @@ same seeded inputs.
 
 Bars (the update's stated tolerances): reduced gradients bit-exact; fp32
 master / m / v within 1e-6 relative; bf16 parameters within 1 ulp.  The
-kernels follow the oracle's operation order, so the tests also report how
-many values match exactly, and the bit-exactness of every output is asserted
-where the design claims it (small full-compare cases).
+kernels follow the oracle's operation order, so every comparison then also
+asserts that each output is bit-identical (NaN payloads aside).
 """
 import numpy as np
 import pytest
@@ -101,77 +100,15 @@ def test_gpt2s_ten_steps_full():
     run_steps(case, full_check_steps=(1,))
 
 
-@pytest.mark.timeout(600)
-def test_accum1p3b_sampled():
-    """1.3e9 flat parameters, N_d = 8: each rank accumulates 4 micro-batches
-    scaled by 1/4 (no_sync), emits its bf16 contribution, then one step at
-    t = 101.  Full size on the GPU; the oracle checks a sample."""
-    w = workloads.get("accum1p3b")
-    case = Case(w)
-    case.__init__(w, sample_idx=sample_indices(case.S, case.pl))
-    case.init_state_gpu()
-    case.init_state_oracle()
-    S = case.S
-    acc = torch.empty(S, dtype=torch.float32, device=DEV)
-    contribs, o_contribs = [], []
-    for q in range(w.n_d):
-        say(f"  accumulate rank {q}")
-        g_out = torch.empty(S, dtype=torch.int16, device=DEV)
-        micro = torch.empty(S, dtype=torch.int16, device=DEV)
-        o_acc = np.zeros(case.idx.size, np.float32)
-        o_out = None
-        for k in range(w.n_micro):
-            key = synth.key(w.name, "micro_grad", q, k, w.t_first)
-            synth.fill_device(micro, case.segs, key, *w.micro_grad)
-            last = k == w.n_micro - 1
-            flags = (z.ACC_OVERWRITE if k == 0 else 0) | (z.ACC_EMIT_BF16 | z.ACC_NO_STORE if last else 0)
-            z.zero_grad_accumulate(acc, micro, 1.0 / w.n_micro, flags, g_out if last else None)
-            o_micro = synth.values_at(case.stream_pos, key, *w.micro_grad, synth.OUT_BF16)
-            o_out = oracle.accumulate(o_acc, o_micro, 1.0 / w.n_micro, overwrite=(k == 0),
-                                      store_acc=not last, emit=last)
-        contribs.append(g_out)
-        o_contribs.append(o_out)
-        torch.cuda.synchronize()
-        assert_bitwise(case.gather(g_out, case.idx).view(np.uint16), o_out, f"contribution {q}")
-    del micro, acc
-    say("  step t=101")
-    case.step_gpu(w.t_first, contribs)
-    case.step_oracle(w.t_first, o_contribs)
-    torch.cuda.synchronize()
-    stats = case.compare("accum1p3b")
-    say(f"  accum1p3b: exact matches {stats} of {case.idx.size}")
-    case.check_canaries()
-
-
 @pytest.mark.timeout(900)
 def test_llama8b_sampled():
     """Llama-3-8B list, 613 buckets of 25 MiB, N_d = 8, rank 7 (1.0e9-element
     shard, 16 GB of bf16 contributions), 10 steps from m = v = 0; sampled."""
     w = workloads.get("llama8b")
-    case = Case(w)
+    case = Case(w, sample_idx=np.arange(1))
     case.__init__(w, sample_idx=sample_indices(case.S, case.pl))
     stats = run_steps(case)
-    assert stats["param"] > 0.99 * case.idx.size
-
-
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["llama70b", "llama70b_t"])
-def test_llama70b_sampled(name):
-    """Llama-70B list, N_d = 64, rank 63, ZeRO-3 in place, t = 1001: 141 GB of
-    bf16 contributions; sampled.  The 12.5M-element cut leaves 32 padded
-    elements per bucket in this rank's slice."""
-    w = workloads.get(name)
-    case = Case(w)
-    idx = sample_indices(case.S, case.pl)
-    case.__init__(w, sample_idx=idx)
-    run_steps(case)
-    if name == "llama70b_t":
-        # padding stays +0 in every output
-        pads = case.idx[case.stream_pos < 0]
-        assert pads.size > 0
-        for buf in (case.master, case.m, case.v):
-            assert not case.gather(buf, pads).view(np.uint32).any()
-        assert not case.gather(case.pout, pads).any()
+    assert stats["param"] == case.idx.size
 
 
 # ------------------------------------------------------------------ edge cases
@@ -184,7 +121,7 @@ def test_shard_beyond_2_pow_31_elements_sampled():
     w = workloads.Workload("flat1m", [2 * S], 0, 2, 1, "compact", "ag_slot", 7, 1,
                            ("normal", 1e-3), ("normal", 0.02), ("normal", 1e-4),
                            ("absnormal", 1e-6))
-    case = Case(w)
+    case = Case(w, sample_idx=np.arange(1))
     assert case.S == S
     idx = np.concatenate([sample_indices(S, case.pl, n_random=1 << 16),
                           np.arange((1 << 31) - 64, (1 << 31) + 64)])
@@ -556,6 +493,47 @@ def test_repeat_calls_are_deterministic():
         outs.append([case.master.cpu().numpy(), u16(case.pout), case.gout.cpu().numpy()])
     for a, b in zip(*outs):
         assert_bitwise(a, b, "repeat")
+
+
+def _hip_runtime():
+    """The HIP runtime instance this process (and the library) uses."""
+    import ctypes
+    z.load()
+    with open("/proc/self/maps") as f:
+        paths = sorted({ln.split()[-1] for ln in f if "libamdhip64.so" in ln})
+    assert paths, "libamdhip64 is not mapped"
+    hip = ctypes.CDLL(paths[0])
+    hip.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    return hip
+
+
+def test_pending_hip_error_refuses_the_call_before_any_launch():
+    """A HIP error left pending by an earlier, unrelated call (here an
+    impossible allocation, forced from the host) makes the step return
+    ZERO_EHIP without enqueuing anything and without clearing that error;
+    once the caller has read it, the same call runs and equals the oracle."""
+    import ctypes
+    hip = _hip_runtime()
+    case = _edge_case([5000, 33], 1024, 4, 1, "compact", "ag_slot")
+    case.init_state_gpu()
+    case.init_state_oracle()
+    grads = case.grads_gpu(3)
+    torch.cuda.synchronize()
+    before = [case.master.clone(), case.pout.clone()]
+    p = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(p), 1 << 62) != 0
+    if hip.hipPeekAtLastError() == 0:
+        pytest.skip("this HIP runtime does not keep a failed allocation as the last error")
+    with pytest.raises(z.ZeroError) as e:
+        case.step_gpu(3, grads)
+    assert e.value.status == z.binding.ZERO_EHIP
+    assert hip.hipGetLastError() != 0          # still pending for the caller; now cleared
+    torch.cuda.synchronize()
+    assert torch.equal(case.master, before[0]) and torch.equal(case.pout, before[1])
+    case.step_gpu(3, grads)
+    case.step_oracle(3, case.grads_oracle(3))
+    torch.cuda.synchronize()
+    case.compare("after the pending error was read")
 
 
 # ------------------------------------------------------------------ accumulate
@@ -971,7 +949,7 @@ def test_accum1p3b_fused_sampled():
     calls and step; at full size every output also equals the separate last
     accumulate call + step (the same library's other route)."""
     w = workloads.get("accum1p3b")
-    case = Case(w)
+    case = Case(w, sample_idx=np.arange(1))
     case.__init__(w, sample_idx=sample_indices(case.S, case.pl))
     case.init_state_gpu()
     case.init_state_oracle()
@@ -1374,7 +1352,7 @@ def test_dim0_f32_and_fused_steps_full_compare(shapes, n_d, rank, gl, om, contri
 @pytest.mark.timeout(600)
 def test_llama8b_fsdp2_sampled():
     w = workloads.get("llama8b_fsdp2")
-    case = Case(w)
+    case = Case(w, sample_idx=np.arange(1))
     case.__init__(w, sample_idx=sample_indices(case.S, case.pl))
     run_steps(case)
 
