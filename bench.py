@@ -250,6 +250,28 @@ def make_timer(stream):
     return timed
 
 
+def make_graph_timer(stream):
+    """fn(stream) -> average milliseconds per replay of a HIP graph holding
+    one fn call (captured on a side stream), so the host's marshalling of
+    many pointers per call is not what is timed."""
+    import torch
+    timed = make_timer(stream)
+
+    def gtimed(fn, reps=10):
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                fn(side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        ms = timed(g.replay, reps=reps)
+        del g
+        return ms
+    return gtimed
+
+
 def aux_kernels(z, synth, workloads, placement):
     """Pack (gpt2s list, one rank's 124M-element flat buffer), the gpt2s
     launch sequence (8 ranks pack, then the step), the no_sync
@@ -284,12 +306,15 @@ def aux_kernels(z, synth, workloads, placement):
     specs = [(f"t{k}", n, torch.int16, float(n)) for k, n in enumerate(w.numel)]
     specs += [("flat", L.padded, torch.int16, float(L.padded))]
     nt = len(w.numel)
-    pack = lambda v: z.zero_bucket_pack(L, [v[f"t{k}"] for k in range(nt)], v["flat"])
+    gtimed = make_graph_timer(torch.cuda.current_stream())
+    pack = lambda v, stream=None: z.zero_bucket_pack(L, [v[f"t{k}"] for k in range(nt)],
+                                                     v["flat"], stream=stream)
     v = buffers(specs, pack)
     for k, segs in enumerate(synth.tensor_segments(w.numel)):
         synth.fill_device(v[f"t{k}"], segs, synth.key(w.name, "grad", 0, 0, 1), *w.grad)
     record("pack_kernel", "gpt2s: 148 tensors -> 124,439,808-element flat buffer, 25 MiB "
-           "buckets", 2 * L.psi + 2 * L.padded, timed(lambda: pack(v)))
+           "buckets (HIP graph replays)", 2 * L.psi + 2 * L.padded,
+           gtimed(lambda st: pack(v, st)))
     del v
     torch.cuda.empty_cache()
 
@@ -305,12 +330,13 @@ def aux_kernels(z, synth, workloads, placement):
     specs += [(k, L.shard, torch.float32, 8.0) for k in ("master", "exp_avg", "exp_avg_sq")]
     specs += [("param_out", L.padded, torch.int16, 2.0)]
 
-    def gpt2s_job(v):
+    def gpt2s_job(v, stream=None):
         for q in range(nd):
-            z.zero_bucket_pack(L, [v[f"t{q}_{k}"] for k in range(nt)], v[f"flat{q}"])
+            z.zero_bucket_pack(L, [v[f"t{q}_{k}"] for k in range(nt)], v[f"flat{q}"],
+                               stream=stream)
         z.zero_shard_step(L, hp, w.t_first, [v[f"flat{q}"] for q in range(nd)], z.GRAD_FLAT,
                           v["master"], v["exp_avg"], v["exp_avg_sq"], v["param_out"],
-                          z.OUT_AG_SLOT)
+                          z.OUT_AG_SLOT, stream=stream)
 
     v = buffers(specs, gpt2s_job)
     tsegs = synth.tensor_segments(w.numel)
@@ -318,8 +344,9 @@ def aux_kernels(z, synth, workloads, placement):
         for k, segs in enumerate(tsegs):
             synth.fill_device(v[f"t{q}_{k}"], segs, synth.key(w.name, "grad", q, 0, 1), *w.grad)
     record("pack_kernel x8 + step_vec_kernel", f"gpt2s step: {nd} ranks pack 148 tensors each, "
-           "then the shard step on rank 7's slices (FLAT, AG slot)",
-           nd * (2 * L.psi + 2 * L.padded) + L.shard * (2 * nd + 26), timed(lambda: gpt2s_job(v)))
+           "then the shard step on rank 7's slices (FLAT, AG slot; HIP graph replays)",
+           nd * (2 * L.psi + 2 * L.padded) + L.shard * (2 * nd + 26),
+           gtimed(lambda st: gpt2s_job(v, st)))
     del v
     torch.cuda.empty_cache()
 
@@ -436,25 +463,35 @@ def next_rows(z, synth, w, L, holder, timed, placement):
         "291 per-tensor slots, 2 table launches", S * (2 * w.n_d + 26), ms)
     # ZeRO-2 stepping bucket by bucket (as each bucket's Reduce-Scatter
     # lands): the same update as one call per bucket range, captured in a
-    # HIP graph so that the host's launch rate is not what is timed
+    # HIP graph so that the host's launch rate is not what is timed.  Single
+    # buckets are also timed with the calls alternating between two streams
+    # (the buckets are disjoint, so the order of their updates is free): one
+    # call's ramp-up then overlaps the previous call's drain.
     nb = L.n_buckets
-    for group in (1, 32):
-        def ranges(stream=None, group=group):
-            for b0 in range(0, nb, group):
+    for group, n_streams in ((1, 1), (1, 2), (32, 1)):
+        def ranges(stream, side, group=group):
+            for k, b0 in enumerate(range(0, nb, group)):
+                st = side[k % len(side)] if side else stream
                 z.zero_shard_step_buckets(L, hp, 6, b0, min(nb, b0 + group), inp.grads,
                                           z.GRAD_COMPACT, *inp.state, inp.pout, z.OUT_AG_SLOT,
-                                          stream=stream)
+                                          stream=st)
         graph = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(graph, stream=side):
-                ranges(stream=side)
-        torch.cuda.current_stream().wait_stream(side)
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        side = [torch.cuda.Stream() for _ in range(n_streams)] if n_streams > 1 else []
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for x in side:
+                    x.wait_stream(cap)
+                ranges(cap, side)
+                for x in side:
+                    cap.wait_stream(x)
+        torch.cuda.current_stream().wait_stream(cap)
         ms = timed(graph.replay, reps=5)
         n_calls = (nb + group - 1) // group
-        row(f"step_buckets_{group}", "step_vec_kernel", f"llama8b step as {n_calls} calls of "
-            f"{group} bucket(s) each (HIP graph)", S * (2 * w.n_d + 26), ms)
+        name = f"step_buckets_{group}" + ("_two_streams" if n_streams > 1 else "")
+        row(name, "step_vec_kernel", f"llama8b step as {n_calls} calls of {group} bucket(s) "
+            f"each on {n_streams} stream(s) (HIP graph)", S * (2 * w.n_d + 26), ms)
         del graph
     # All-Gather local part: the 8 bf16 shards (the contribution buffers
     # stand in for them) into the 8.03e9-element flat buffer
@@ -644,6 +681,69 @@ def second_config(z, synth, name, args, stream):
             "placement": used, "placement_tuning": tuning, "roofline": roof, "cpu_baseline": cpu}
 
 
+def placement_sweep(z, w, L, sweep, pool_gib=240, step_gib=8, reps=4):
+    """Where the step's buffers sit in HBM, swept (printed as markdown).
+    shifts: one large pool; the buffers laid out packed one after another,
+    or by zero_placement_plan, and the whole arrangement moved through the
+    pool in steps of step_gib.  poolsize: the planned arrangement at the
+    start of pools of growing size.  Values are not initialised (timing
+    only); every timed call is a whole shard step."""
+    import torch
+    from fsdp_sharded_optimizer_step_amd import binding
+    from fsdp_sharded_optimizer_step_amd import placement as zp
+    GiB = 1 << 30
+    hp = z.AdamW(**w.hp)
+    om = z.OUT_AG_SLOT if w.out_mode == "ag_slot" else z.OUT_SHARD
+    gl = z.GRAD_COMPACT if w.grad_layout == "compact" else z.GRAD_FLAT
+    specs = zp.step_specs(L, grad_layout=gl, out_mode=om)
+    nbytes = [n * torch.empty((), dtype=dt).element_size() for _, n, dt, _ in specs]
+    plan, need = binding.zero_placement_plan(nbytes, [sp[3] for sp in specs], zp.LANE_BYTES,
+                                             zp.N_LANES, zp.ALIGN)
+    packed, off = [], 0
+    for n in nbytes:
+        packed.append(off)
+        off = (off + n + zp.ALIGN - 1) // zp.ALIGN * zp.ALIGN
+    packed_need = off
+    stream = torch.cuda.current_stream()
+    timed = make_timer(stream)
+    nd, bpe = L.n_d, 2 * L.n_d + 26
+
+    def step_ms(pool, offs, shift):
+        v = []
+        for (_, _, dt, _), o, b in zip(specs, offs, nbytes):
+            assert 0 <= o + shift and o + shift + b <= pool.numel()
+            v.append(pool[o + shift:o + shift + b].view(dt))
+        fn = lambda: z.zero_shard_step(L, hp, w.t_first, v[:nd], gl, v[nd], v[nd + 1],
+                                       v[nd + 2], v[nd + 3], om)
+        return min(timed(fn, reps=reps) for _ in range(2))
+
+    print(f"workload {w.name}: S = {L.shard}, N_d = {nd}, {bpe} bytes per element; planned "
+          f"arrangement {need / GiB:.1f} GiB, packed {packed_need / GiB:.1f} GiB; kernel "
+          f"sources {kernel_hash()}\n")
+    if sweep == "shifts":
+        pool = torch.empty(pool_gib * GiB, dtype=torch.uint8, device="cuda:0")
+        print(f"pool of {pool_gib} GiB; step ms (TB/s) with the arrangement shifted by:\n")
+        print("| shift GiB | packed ms | packed TB/s | planned ms | planned TB/s |")
+        print("|---|---|---|---|---|")
+        last = min(pool_gib * GiB - need, pool_gib * GiB - packed_need)
+        for sh in range(0, last // GiB + 1, step_gib):
+            a = step_ms(pool, packed, sh * GiB)
+            b = step_ms(pool, plan, sh * GiB)
+            print(f"| {sh} | {a:.3f} | {L.shard * bpe / a / 1e9:.2f} | {b:.3f} | "
+                  f"{L.shard * bpe / b / 1e9:.2f} |", flush=True)
+    else:
+        print("planned arrangement at the start of a pool of the plan's size + extra:\n")
+        print("| extra GiB | pool GiB | step ms | TB/s |")
+        print("|---|---|---|---|")
+        for extra in range(0, 97, step_gib):
+            pool = torch.empty(need + extra * GiB, dtype=torch.uint8, device="cuda:0")
+            ms = step_ms(pool, plan, 0)
+            print(f"| {extra} | {(need + extra * GiB) / GiB:.1f} | {ms:.3f} | "
+                  f"{L.shard * bpe / ms / 1e9:.2f} |", flush=True)
+            del pool
+            torch.cuda.empty_cache()
+
+
 def workloads_mod():
     from synth import workloads
     return workloads
@@ -668,6 +768,9 @@ def main():
                          "same pool at shift 0; separate: one torch allocation per buffer")
     ap.add_argument("--all-configs", action="store_true",
                     help="time the step of every shard workload instead (one JSON line)")
+    ap.add_argument("--placement-sweep", choices=["shifts", "poolsize"],
+                    help="instead: time the step of --workload with its buffers at many places "
+                         "in HBM (markdown table)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (3 times): the known-size "
                          "reference for scaling HBM byte counters")
@@ -694,6 +797,10 @@ def main():
     from synth import workloads
 
     z.load()
+    if args.placement_sweep:
+        w = workloads.get(args.workload)
+        placement_sweep(z, w, z.Layout(w.numel, w.cap, w.n_d, w.rank), args.placement_sweep)
+        return
     if args.all_configs:
         print(json.dumps({"per_config": all_configs(z, synth, workloads, args.steps,
                                                     args.warmup, args.placement)}), flush=True)

@@ -32,24 +32,33 @@ using namespace zs;
 struct Piece {
   const uint16_t* src;  // nullptr: write zeros (bucket padding)
   int64_t dst;          // element offset in the flat buffer
-  int64_t n;            // element count
+  int64_t n;            // element count (at most kMaxPieceElems)
   int32_t head;         // vector pieces: elements (< 8) before the destination is 16-byte aligned
   int32_t vec;          // 1: source and destination share 16-byte phase (or zeros)
 };
-// 96 pieces per launch keep the kernel arguments under 4 KB (GPT-2's 148
-// tensors in 10 buckets take 2 launches)
-constexpr int kPiecesPerLaunch = 96;
+// A launch carries its pieces in the kernel arguments, 24 bytes each
+// (source, destination with the head and vector flag in its top bits,
+// length, first tile): 169 pieces fit in 4 KB, so GPT-2's 148 tensors and
+// 10 bucket pads go in one launch instead of two.
+constexpr int kPiecesPerLaunch = 169;
 constexpr int kPackThreads = 256;
+// pieces longer than this are cut (a multiple of 8 elements, so the parts
+// keep the 16-byte phase of the whole)
+constexpr int64_t kMaxPieceElems = (int64_t)1 << 30;
+constexpr int kDstBits = 56;
+constexpr uint64_t kDstMask = ((uint64_t)1 << kDstBits) - 1;
 // Tiles of 512 vectors (4096 elements) and non-temporal accesses: the
 // fastest of 3 tile sizes x 2 cache hints measured on MI355X for GPT-2's
 // buckets (84 us against 98 us for 1024-vector tiles with ordinary accesses).
 constexpr int64_t kTileVecs = kPackThreads * 2;   // 8-element vectors per tile
 constexpr int64_t kTileElems = kPackThreads * 4;  // elements per tile, scalar pieces
 struct PackArgs {
-  Piece p[kPiecesPerLaunch];
-  int32_t tile0[kPiecesPerLaunch + 1];  // first tile of each piece; tile0[n] = total
+  const uint16_t* src[kPiecesPerLaunch];
+  uint64_t dst[kPiecesPerLaunch];       // offset | head << 56 | vec << 60
+  uint32_t n[kPiecesPerLaunch];
+  int32_t tile0[kPiecesPerLaunch + 1];  // first tile of each piece; tile0[count] = total
   uint16_t* out;
-  int32_t n;
+  int32_t count;
   int32_t tile_base;  // first tile of this launch
 };
 static_assert(sizeof(PackArgs) <= 4096, "kernel arguments");
@@ -65,29 +74,33 @@ int64_t piece_tiles(const Piece& pc) {
 
 __global__ void __launch_bounds__(kPackThreads) pack_kernel(const PackArgs A) {
   const int64_t tile = (int64_t)A.tile_base + blockIdx.x;
-  int lo = 0, hi = A.n;
+  int lo = 0, hi = A.count;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (A.tile0[mid] <= tile) lo = mid;
     else hi = mid;
   }
-  const Piece pc = A.p[lo];
+  const uint16_t* src = A.src[lo];
+  const uint64_t dw = A.dst[lo];
+  const int64_t n = A.n[lo];
+  const int32_t head = (int32_t)((dw >> kDstBits) & 15u);
+  const bool vec = ((dw >> (kDstBits + 4)) & 1u) != 0;
   const int64_t t = tile - A.tile0[lo];
   const int64_t ntile = A.tile0[lo + 1] - A.tile0[lo];
-  uint16_t* d = A.out + pc.dst;
-  const bool zeros = pc.src == nullptr;
-  if (!pc.vec) {
-    const int64_t e0 = t * kTileElems, e1 = std::min(pc.n, e0 + kTileElems);
-    for (int64_t e = e0 + threadIdx.x; e < e1; e += kPackThreads) d[e] = pc.src[e];
+  uint16_t* d = A.out + (int64_t)(dw & kDstMask);
+  const bool zeros = src == nullptr;
+  if (!vec) {
+    const int64_t e0 = t * kTileElems, e1 = std::min(n, e0 + kTileElems);
+    for (int64_t e = e0 + threadIdx.x; e < e1; e += kPackThreads) d[e] = src[e];
     return;
   }
-  const int64_t nv = (pc.n - pc.head) >> 3;
-  const int64_t tail0 = pc.head + (nv << 3);
-  if (t == 0 && threadIdx.x < pc.head) d[threadIdx.x] = zeros ? (uint16_t)0 : pc.src[threadIdx.x];
-  if (t == ntile - 1 && threadIdx.x < pc.n - tail0)
-    d[tail0 + threadIdx.x] = zeros ? (uint16_t)0 : pc.src[tail0 + threadIdx.x];
-  u32x4* dv = (u32x4*)(d + pc.head);
-  const u32x4* sv = zeros ? nullptr : (const u32x4*)(pc.src + pc.head);
+  const int64_t nv = (n - head) >> 3;
+  const int64_t tail0 = head + (nv << 3);
+  if (t == 0 && threadIdx.x < head) d[threadIdx.x] = zeros ? (uint16_t)0 : src[threadIdx.x];
+  if (t == ntile - 1 && threadIdx.x < n - tail0)
+    d[tail0 + threadIdx.x] = zeros ? (uint16_t)0 : src[tail0 + threadIdx.x];
+  u32x4* dv = (u32x4*)(d + head);
+  const u32x4* sv = zeros ? nullptr : (const u32x4*)(src + head);
   const int64_t v0 = t * kTileVecs, v1 = std::min(nv, v0 + kTileVecs);
   for (int64_t v = v0 + threadIdx.x; v < v1; v += kPackThreads)
     st_stream<true>(dv + v, zeros ? u32x4{0u, 0u, 0u, 0u} : ld_stream<true>(sv + v));
@@ -205,10 +218,14 @@ int zero_bucket_pack(const zero_layout* L, const uint16_t* const* tensor_grads,
       if (a >= z) continue;
       const uint16_t* src = tensor_grads[t];
       if (!src) return ZERO_EINVAL;
-      pieces.push_back(Piece{src + (a - L->tensor_off[t]), base + (a - x0), z - a, 0, 0});
+      for (int64_t u = a; u < z; u += kMaxPieceElems)
+        pieces.push_back(Piece{src + (u - L->tensor_off[t]), base + (u - x0),
+                               std::min(kMaxPieceElems, z - u), 0, 0});
     }
     const int64_t pad = L->bucket_padded(b) - L->bucket_len(b);
-    if (pad > 0) pieces.push_back(Piece{nullptr, base + L->bucket_len(b), pad, 0, 0});
+    for (int64_t u = 0; u < pad; u += kMaxPieceElems)
+      pieces.push_back(Piece{nullptr, base + L->bucket_len(b) + u,
+                             std::min(kMaxPieceElems, pad - u), 0, 0});
   }
   // vector eligibility and head peel (destination alignment) per piece
   for (Piece& pc : pieces) {
@@ -230,17 +247,23 @@ int zero_bucket_pack(const zero_layout* L, const uint16_t* const* tensor_grads,
   }
   if (pieces.empty()) return ZERO_OK;
   if (hip_error_pending()) return ZERO_EHIP;
+  // destinations fit the 56-bit field (flat buffers far below 2^56 elements)
+  if (L->P >= (int64_t)kDstMask) return ZERO_ERANGE;
   for (size_t p0 = 0; p0 < pieces.size(); p0 += kPiecesPerLaunch) {
     PackArgs A;
     A.out = flat_out;
-    A.n = (int32_t)std::min<size_t>(kPiecesPerLaunch, pieces.size() - p0);
+    A.count = (int32_t)std::min<size_t>(kPiecesPerLaunch, pieces.size() - p0);
     int64_t tiles = 0;
-    for (int k = 0; k < A.n; ++k) {
-      A.p[k] = pieces[p0 + k];
+    for (int k = 0; k < A.count; ++k) {
+      const Piece& pc = pieces[p0 + k];
+      A.src[k] = pc.src;
+      A.dst[k] = (uint64_t)pc.dst | ((uint64_t)pc.head << kDstBits) |
+                 ((uint64_t)(pc.vec ? 1 : 0) << (kDstBits + 4));
+      A.n[k] = (uint32_t)pc.n;
       A.tile0[k] = (int32_t)tiles;
-      tiles += piece_tiles(A.p[k]);
+      tiles += piece_tiles(pc);
     }
-    A.tile0[A.n] = (int32_t)tiles;
+    A.tile0[A.count] = (int32_t)tiles;
     for (int64_t t0 = 0; t0 < tiles; t0 += kMaxBlocks) {
       A.tile_base = (int32_t)t0;
       const unsigned grid = (unsigned)std::min(kMaxBlocks, tiles - t0);

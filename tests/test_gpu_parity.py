@@ -255,6 +255,27 @@ def test_tuned_step_pool_times_the_step_at_each_shift():
     assert len(pool.grads) == 8 and pool["param_out"].numel() == L.shard
 
 
+def test_tuned_step_pool_times_the_call_its_buffers_are_for(monkeypatch):
+    """A pool holding fp32 accumulators is placed by timing the fused step
+    (zero_shard_step_accumulate) on them, with the reduced gradient written
+    when the pool holds one."""
+    from fsdp_sharded_optimizer_step_amd import placement as zp
+    calls = []
+    real = zp.zero_shard_step_accumulate
+
+    def spy(layout, hp, t, acc, micro, *a):
+        calls.append((len(acc), len(micro), a[-1] is not None))
+        return real(layout, hp, t, acc, micro, *a)
+
+    monkeypatch.setattr(zp, "zero_shard_step_accumulate", spy)
+    L = z.Layout([300_001, 77], 65_536, 4, 3)
+    pool = zp.tuned_step_pool(L, z.AdamW(), 1, z.GRAD_COMPACT, z.OUT_SHARD, slack=2 << 20,
+                              lane_bytes=1 << 20, align=256, shift_step=1 << 20,
+                              accumulators=True, reduced_grad=True)
+    assert len(pool.tuning) == 3 and calls
+    assert all(c == (4, 4, True) for c in calls)
+
+
 def test_tuned_step_pool_falls_back_to_a_search_that_fits(monkeypatch):
     """With no explicit slack the helper tries its searches in order: one
     whose pool cannot be allocated is skipped for the next."""
@@ -667,6 +688,34 @@ def test_bucket_ranges_in_any_order_equal_the_oracle(numel, cap, n_d, rank, gl, 
         assert_bitwise(a.cpu().numpy(), b, "state")
     pos = case.flat_pos if om == "ag_slot" else np.arange(case.S)
     assert_bitwise(u16(case.pout)[pos], case.o_p, "param")
+    case.check_canaries(n_probe=4096)
+
+
+def test_single_buckets_on_two_streams_equal_the_oracle():
+    """ZeRO-2 call pattern: every bucket stepped on its own, the calls
+    alternating between two streams (buckets are disjoint, so they may run
+    concurrently), three steps: the oracle's whole-shard step bit for bit.
+    The buckets are large enough for the small-region grid (one chunk per
+    wave, several blocks per CU)."""
+    case = _edge_case([10_000_003, 5_555_555, 77], 8_000_000, 8, 5, "compact", "ag_slot")
+    case.init_state_gpu()
+    case.init_state_oracle()
+    main = torch.cuda.current_stream()
+    side = [torch.cuda.Stream(), torch.cuda.Stream()]
+    gl, om = z.GRAD_COMPACT, z.OUT_AG_SLOT
+    for t in (1, 2, 3):
+        grads = case.grads_gpu(t)
+        for x in side:
+            x.wait_stream(main)
+        for b in range(case.L.n_buckets):
+            z.zero_shard_step_buckets(case.L, case.hp_z, t, b, b + 1, grads, gl, case.master,
+                                      case.m, case.v, case.pout, om, case.gout,
+                                      stream=side[b % 2])
+        for x in side:
+            main.wait_stream(x)
+        case.step_oracle(t, case.grads_oracle(t))
+    torch.cuda.synchronize()
+    case.compare("single buckets on two streams")
     case.check_canaries(n_probe=4096)
 
 
