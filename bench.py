@@ -106,16 +106,30 @@ def step_call(z, L, hp, t, grad_layout, out_mode, fused=False):
     return call
 
 
+def mix_choose(L):
+    """views -> milliseconds of the same-mix probe on the step's buffers: the
+    placement search of the timed workloads, so that the step kernel's
+    dispatches in a kernel trace are the warm-up and the timed calls only."""
+    import measure
+
+    def choose(v):
+        g = [v[f"g{q}"] for q in range(L.n_d)]
+        return measure.mix_ms(g, [v["master"], v["exp_avg"], v["exp_avg_sq"]], v["param_out"],
+                              L.shard)
+    return choose
+
+
 def make_inputs(z, synth, w, L, placement="tuned", grad_dtype=None, accumulators=False,
-                grad_micro=0, call=None, tune=((TUNE_SLACK, 4 << 30),)):
+                grad_micro=0, call=None, tune=((TUNE_SLACK, 4 << 30),), choose=None):
     """Buffers for workload w on layout L filled with the workload's seeded
     values (contributions keyed (grad, rank, grad_micro, t_first); FLAT ones
     over the padded flat buffer), the output zeroed.  placement "tuned": one
     pool laid out by zero_placement_plan with spare bytes, the arrangement's
     start chosen by timing `call` (views -> one call) at shifts over the
     spare room (`tune`: (spare bytes, shift step) pairs tried in order until
-    a pool fits); "planned": the same pool without spare bytes; "separate":
-    one torch allocation per buffer."""
+    a pool fits), or by `choose` (views -> milliseconds) when given;
+    "planned": the same pool without spare bytes; "separate": one torch
+    allocation per buffer."""
     import torch
     from fsdp_sharded_optimizer_step_amd import placement as zp
     dev = torch.device("cuda:0")
@@ -128,8 +142,9 @@ def make_inputs(z, synth, w, L, placement="tuned", grad_dtype=None, accumulators
         raise ValueError(placement)
     pool = None
     if placement in ("tuned", "planned"):
-        choose = None
-        if placement == "tuned":
+        if placement != "tuned":
+            choose = None
+        elif choose is None:
             if call is None:
                 call = step_call(z, L, z.AdamW(**w.hp), w.t_first, gl, om, fused=accumulators)
             timed = make_timer(torch.cuda.current_stream())
@@ -313,8 +328,29 @@ def aux_kernels(z, synth, workloads, placement):
     for k, segs in enumerate(synth.tensor_segments(w.numel)):
         synth.fill_device(v[f"t{k}"], segs, synth.key(w.name, "grad", 0, 0, 1), *w.grad)
     record("pack_kernel", "gpt2s: 148 tensors -> 124,439,808-element flat buffer, 25 MiB "
-           "buckets (HIP graph replays)", 2 * L.psi + 2 * L.padded,
-           gtimed(lambda st: pack(v, st)))
+           "buckets (HIP graph replays; the same 249 MB of sources every replay)",
+           2 * L.psi + 2 * L.padded, gtimed(lambda st: pack(v, st)))
+    del v
+    torch.cuda.empty_cache()
+    # the 8 simulated ranks' packs, each from its own 148 tensors (2 GB of
+    # sources in all, so none is still held by the 256 MB MALL when read)
+    nd = w.n_d
+    specs = [(f"t{q}_{k}", n, torch.int16, float(n)) for q in range(nd)
+             for k, n in enumerate(w.numel)]
+    specs += [(f"flat{q}", L.padded, torch.int16, float(L.padded)) for q in range(nd)]
+
+    def packs(v, stream=None):
+        for q in range(nd):
+            z.zero_bucket_pack(L, [v[f"t{q}_{k}"] for k in range(nt)], v[f"flat{q}"],
+                               stream=stream)
+
+    v = buffers(specs, packs)
+    for q in range(nd):
+        for k, segs in enumerate(synth.tensor_segments(w.numel)):
+            synth.fill_device(v[f"t{q}_{k}"], segs, synth.key(w.name, "grad", q, 0, 1), *w.grad)
+    record("pack_kernel x8", f"gpt2s: {nd} ranks each pack their own 148 tensors into their "
+           "own flat buffer (HIP graph replays)", nd * (2 * L.psi + 2 * L.padded),
+           gtimed(lambda st: packs(v, st)))
     del v
     torch.cuda.empty_cache()
 
@@ -643,11 +679,12 @@ def roofline_block(w, S, kernel_ms):
             "kernel_hash": kernel_hash()}
 
 
-def placement_info(inp):
+def placement_info(inp, searched_with="the same-mix probe (measure/stream_ceiling.hip)"):
     if inp.pool is None:
         return "separate", None
     return "tuned", {"pool_GiB": inp.pool.nbytes / 2**30,
                      "chosen_shift_GiB": inp.pool.shift / 2**30,
+                     "searched_with": searched_with,
                      "ms_by_shift_GiB": [[sh / 2**30, ms] for sh, ms in inp.pool.tuning]}
 
 
@@ -660,7 +697,8 @@ def second_config(z, synth, name, args, stream):
     S, P = L.shard, L.padded
     print(f"# workload {w.name}: S={S} P={P} N_d={w.n_d} buckets={L.n_buckets}", file=sys.stderr,
           flush=True)
-    inp, segs = make_inputs(z, synth, w, L, args.placement, tune=MAIN_TUNE)
+    inp, segs = make_inputs(z, synth, w, L, args.placement, tune=MAIN_TUNE,
+                            choose=mix_choose(L) if w.grad_layout == "compact" else None)
     used, tuning = placement_info(inp)
     ms_per_step, kernel_ms, _ = time_steps(z, w, L, inp, args.steps, args.warmup, stream)
     roof = roofline_block(w, S, kernel_ms)
@@ -810,8 +848,11 @@ def main():
     S, P = L.shard, L.padded
     print(f"# workload {w.name}: S={S} P={P} N_d={w.n_d} buckets={L.n_buckets}", file=sys.stderr,
           flush=True)
-    inp, segs = make_inputs(z, synth, w, L, args.placement, tune=MAIN_TUNE)
-    placement_used, tuning = placement_info(inp)
+    inp, segs = make_inputs(z, synth, w, L, args.placement, tune=MAIN_TUNE,
+                            choose=mix_choose(L) if w.grad_layout == "compact" else None)
+    placement_used, tuning = placement_info(
+        inp, "the same-mix probe (measure/stream_ceiling.hip)" if w.grad_layout == "compact"
+        else "the step")
     if placement_used == "tuned" and args.placement != "tuned":
         placement_used = args.placement
     hp = z.AdamW(**w.hp)

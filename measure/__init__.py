@@ -94,3 +94,33 @@ def stream_probes(grads, state, out, n: int, reps: int = 5):
                     best = (gbps, {"blocks_per_cu": bpc, "nontemporal": bool(nt), "ms": ms})
         res[name] = {"GBps": best[0], "config": best[1]}
     return res
+
+
+def mix_ms(grads, state, out, n: int, reps: int = 4):
+    """Milliseconds per launch of the same-mix kernel (every access
+    non-temporal, one 256-thread block per CU, the step's chunk mapping) on
+    the given buffers, after one untimed launch.  It moves the step's bytes
+    in the step's pattern, so it ranks placements of the step's buffers as
+    the step does (measured: the same best shift of the Llama-3-8B pool, and
+    one within 0.04 % of the step's best for Llama-70B), while the step's own
+    kernel stays out of the search."""
+    import torch
+    lib = _load()
+    nd = len(grads)
+    g = (C.c_void_p * nd)(*[t.data_ptr() for t in grads])
+    s = (C.c_void_p * 3)(*[t.data_ptr() for t in state])
+    n = n // 512 * 512
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    args = (g, nd, s, out.data_ptr(), n, cus, 7, stream.cuda_stream)
+    if lib.stream_ceiling_launch(*args) != 0:
+        raise RuntimeError("stream_ceiling_launch failed")
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        lib.stream_ceiling_launch(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
