@@ -323,6 +323,14 @@ int zero_shard_step_accumulate(const zero_layout* layout, const zero_adamw* hp, 
  * once, in any grouping and order, gives the same bits as one
  * zero_shard_step_ex call.
  *
+ * Calls on disjoint bucket ranges touch disjoint memory, so they may also
+ * run concurrently on different streams.  Consecutive kernels of one stream
+ * do not overlap, so one call per bucket pays each launch's ramp-up and
+ * drain in turn: measured on MI355X for the Llama-3-8B shard (613 calls of
+ * one 25 MiB bucket), 57 % of the HBM peak on one stream against 76-77 %
+ * with the calls alternating between two streams (79 % for the whole shard
+ * in one call).
+ *
  * All buffers are the full-size ones of zero_shard_step_ex (contributions of
  * S or P values, S-element state, S- or P-element output); only the slices
  * of the named buckets are read and written.  For a dim-0 layout a bucket is
