@@ -95,6 +95,32 @@ def test_gpt2s_pack_matches_oracle():
     assert_bitwise(u16(flat), exp, "packed flat buffer")
 
 
+@pytest.mark.timeout(300)
+def test_pack_cuts_pieces_longer_than_2_pow_30():
+    """A 3-element tensor, then one of 2^30 + 4103 elements in the same
+    bucket (the pack cuts pieces at 2^30 elements, keeping the 16-byte
+    phase), and the bucket's padding at N_d = 8.  The long tensor starts 6
+    bytes into a 16-byte line of the flat buffer; its source is placed at the
+    same phase (vector pieces with a 5-element head) or at another one
+    (element-wise pieces).  The flat buffer equals the tensors in order,
+    padding +0."""
+    n0 = (1 << 30) + 4103
+    L = z.Layout([3, n0], 0, 8, 3)
+    P = L.padded
+    head = torch.tensor([7, -9, 11], dtype=torch.int16, device=DEV)
+    for off in (3, 1):
+        src = torch.empty(n0 + 16, dtype=torch.int16, device=DEV)[off:off + n0]
+        src.copy_(torch.arange(n0, dtype=torch.int32, device=DEV).to(torch.int16))
+        flat = torch.full((P,), CANARY, dtype=torch.int16, device=DEV)
+        z.zero_bucket_pack(L, [head, src], flat)
+        torch.cuda.synchronize()
+        assert torch.equal(flat[:3], head)
+        assert torch.equal(flat[3:3 + n0], src), f"long tensor (source offset {off})"
+        assert not flat[3 + n0:].any(), "bucket padding is +0"
+        del src, flat
+        torch.cuda.empty_cache()
+
+
 def test_gpt2s_ten_steps_full():
     case = Case(workloads.get("gpt2s"))
     run_steps(case, full_check_steps=(1,))

@@ -85,14 +85,24 @@ def _outputs(case, c0, c1):
             p)
 
 
-def run_whole_shard(name):
+def run_whole_shard(name, f32=False):
+    """One step of workload `name` on the GPU, then every element against the
+    oracle; `f32`: binary32 contributions (the generator's values unrounded),
+    stepped by zero_shard_step_ex with ZERO_DTYPE_F32."""
     w = workloads.get(name)
     assert w.grad_layout == "compact"
     case = Case(w, sample_idx=np.arange(1))
     S, t = case.S, w.t_first
-    say(f"  {name}: S={S} N_d={w.n_d} t={t}")
+    say(f"  {name}: S={S} N_d={w.n_d} t={t}" + (" fp32 contributions" if f32 else ""))
     case.init_state_gpu()
-    grads = case.grads_gpu(t)
+    if f32:
+        grads = []
+        for q in range(w.n_d):
+            g = torch.empty(S, dtype=torch.float32, device=DEV)
+            synth.fill_device(g, case.segs, synth.key(w.name, "grad", q, 0, t), *w.grad)
+            grads.append(g)
+    else:
+        grads = case.grads_gpu(t)
     pre = [x.clone() for x in (case.master, case.m, case.v)]
     case.step_gpu(t, grads)
     torch.cuda.synchronize()
@@ -105,12 +115,12 @@ def run_whole_shard(name):
     t0 = time.time()
     for c0 in range(0, S, CHUNK):
         c1 = min(S, c0 + CHUNK)
-        G = [_host(g[c0:c1]).view(np.uint16) for g in grads]
+        G = [_host(g[c0:c1]) if f32 else _host(g[c0:c1]).view(np.uint16) for g in grads]
         st = [_host(x[c0:c1]) for x in pre]
-        _pin_inputs(case, c0, c1, G, gkeys, synth.OUT_BF16, rng)
+        _pin_inputs(case, c0, c1, G, gkeys, synth.OUT_F32 if f32 else synth.OUT_BF16, rng)
         _pin_inputs(case, c0, c1, st, skeys, synth.OUT_F32, rng)
-        o_p, o_g = oracle.shard_step(G, *st, case.hp_o, t, want_grad=True,
-                                     nthreads=synth.HOST_THREADS)
+        step = oracle.shard_step_f32 if f32 else oracle.shard_step
+        o_p, o_g = step(G, *st, case.hp_o, t, want_grad=True, nthreads=synth.HOST_THREADS)
         _compare_chunk(case, c0, c1, _outputs(case, c0, c1), (*st, o_p, o_g),
                        f"{name} [{c0}, {c1})")
         if (c0 // CHUNK) % 16 == 0:
@@ -136,6 +146,14 @@ def test_whole_shard_equals_oracle(name):
                                                    else np.uint16).any()
     if case.w.out_mode == "ag_slot":
         case.check_canaries()
+
+
+@pytest.mark.timeout(900)
+def test_whole_shard_with_fp32_contributions_equals_oracle():
+    """The Llama-3-8B shard with binary32 contributions (a Reduce-Scatter in
+    fp32, 58 bytes per element), one step, every element."""
+    case = run_whole_shard("llama8b", f32=True)
+    case.check_canaries()
 
 
 @pytest.mark.timeout(900)
