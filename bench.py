@@ -532,7 +532,7 @@ def next_rows(z, synth, w, L, holder, timed, placement):
     # All-Gather local part: the 8 bf16 shards (the contribution buffers
     # stand in for them) into the 8.03e9-element flat buffer
     ms = timed(lambda: z.zero_gather_params(L, inp.grads, inp.pout))
-    row("gather", "gather_kernel", "llama8b: 8 rank shards -> 8,030,261,248-element flat "
+    row("gather", "gather_table_kernel", "llama8b: 8 rank shards -> 8,030,261,248-element flat "
         "buffer", 4 * P, ms)
     # the same two movements for the per-parameter (dim-0) layout: its
     # gather (one table launch per 48 tensors) and a re-cut of its bf16
