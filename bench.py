@@ -128,7 +128,8 @@ def make_inputs(z, synth, w, L, placement="tuned", grad_dtype=None, accumulators
     start chosen by timing `call` (views -> one call) at shifts over the
     spare room (`tune`: (spare bytes, shift step) pairs tried in order until
     a pool fits), or by `choose` (views -> milliseconds) when given;
-    "planned": the same pool without spare bytes; "separate": one torch
+    "planned": the same pool without spare bytes; "compact": three lanes
+    just large enough for the buffers, no spare bytes; "separate": one torch
     allocation per buffer."""
     import torch
     from fsdp_sharded_optimizer_step_amd import placement as zp
@@ -138,10 +139,18 @@ def make_inputs(z, synth, w, L, placement="tuned", grad_dtype=None, accumulators
     om = z.OUT_AG_SLOT if w.out_mode == "ag_slot" else z.OUT_SHARD
     specs = zp.step_specs(L, grad_dtype=grad_dtype, grad_layout=gl, out_mode=om,
                           accumulators=accumulators)
-    if placement not in ("tuned", "planned", "separate"):
+    if placement not in ("tuned", "planned", "compact", "separate"):
         raise ValueError(placement)
     pool = None
-    if placement in ("tuned", "planned"):
+    if placement == "compact":
+        # three lanes just large enough for the buffers (a pool of about
+        # 1.2x their size), at the allocation's own start: no spare room,
+        # no timed search
+        total = sum(n * torch.empty((), dtype=dt).element_size() for _, n, dt, _ in specs)
+        lane = -(-total // (3 << 30)) << 30
+        pool = zp.Pool(specs, device=dev, lane_bytes=lane)
+        views = pool.views
+    elif placement in ("tuned", "planned"):
         if placement != "tuned":
             choose = None
         elif choose is None:
@@ -682,6 +691,8 @@ def roofline_block(w, S, kernel_ms):
 def placement_info(inp, searched_with="the same-mix probe (measure/stream_ceiling.hip)"):
     if inp.pool is None:
         return "separate", None
+    if not inp.pool.tuning:
+        return "pool", {"pool_GiB": inp.pool.nbytes / 2**30, "searched_with": None}
     return "tuned", {"pool_GiB": inp.pool.nbytes / 2**30,
                      "chosen_shift_GiB": inp.pool.shift / 2**30,
                      "searched_with": searched_with,
@@ -800,10 +811,12 @@ def main():
                          "two Llama-70B shards, N_d = 64, in the same JSON line)")
     ap.add_argument("--blocks", type=int, default=0)
     ap.add_argument("--threads", type=int, default=0)
-    ap.add_argument("--placement", default="tuned", choices=["tuned", "planned", "separate"],
+    ap.add_argument("--placement", default="tuned",
+                    choices=["tuned", "planned", "compact", "separate"],
                     help="tuned: the step's buffers in one pool laid out by zero_placement_plan, "
-                         "its start chosen by timing the step at a few shifts; planned: the "
-                         "same pool at shift 0; separate: one torch allocation per buffer")
+                         "its start chosen by timing the same-mix probe at a few shifts; "
+                         "planned: the same pool at shift 0; compact: lanes just large enough "
+                         "for the buffers, at shift 0; separate: one torch allocation per buffer")
     ap.add_argument("--all-configs", action="store_true",
                     help="time the step of every shard workload instead (one JSON line)")
     ap.add_argument("--placement-sweep", choices=["shifts", "poolsize"],
@@ -853,7 +866,7 @@ def main():
     placement_used, tuning = placement_info(
         inp, "the same-mix probe (measure/stream_ceiling.hip)" if w.grad_layout == "compact"
         else "the step")
-    if placement_used == "tuned" and args.placement != "tuned":
+    if placement_used != "separate":
         placement_used = args.placement
     hp = z.AdamW(**w.hp)
     gl = z.GRAD_COMPACT if w.grad_layout == "compact" else z.GRAD_FLAT
@@ -885,10 +898,11 @@ def main():
     holder.clear()
     torch.cuda.empty_cache()
     # the same step on placements that need no timed search: one torch
-    # allocation per buffer, and the planned pool at its start
+    # allocation per buffer, the planned pool at its start, and a pool of
+    # about 1.2x the buffers (lanes just large enough) at its start
     other = {}
     if not args.no_aux:
-        for alt in ("separate", "planned"):
+        for alt in ("separate", "planned", "compact"):
             inp, _ = make_inputs(z, synth, w, L, alt)
             ms_alt = make_timer(stream)(lambda: z.zero_shard_step(
                 L, hp, t, inp.grads, gl, *inp.state, inp.pout, om), reps=10)
