@@ -222,19 +222,19 @@ def cpu_baseline(w, segs, S, target_s=12.0):
         return n, G, st
 
     hp = oracle.AdamW(**w.hp)
-    n, G, st = sample_inputs(min(S, 1 << 20))
+    # the sample: 2^29 / N_d contiguous shard elements (64M at N_d = 8, 8M
+    # at N_d = 64), stepped repeatedly (t advancing) until about target_s of
+    # CPU work has been timed; the number of steps comes from one untimed
+    # step of the same sample
+    n = int(min(S, (1 << 29) // w.n_d))
+    n, G, st = sample_inputs(n)
     t0 = time.perf_counter()
     oracle.shard_step(G, *st, hp, w.t_first, nthreads=threads)
     pilot = max(1e-6, time.perf_counter() - t0)
-    # the sample: 2^29 / N_d contiguous shard elements (64M at N_d = 8),
-    # stepped repeatedly (t advancing) until about target_s of CPU work has
-    # been timed
-    n = int(min(S, (1 << 29) // w.n_d))
-    reps = max(1, int(round(target_s / (pilot * n / (1 << 20)))))
-    n, G, st = sample_inputs(n)
+    reps = max(1, int(round(target_s / pilot)))
     t0 = time.perf_counter()
     for k in range(reps):
-        oracle.shard_step(G, *st, hp, w.t_first + k, nthreads=threads)
+        oracle.shard_step(G, *st, hp, w.t_first + 1 + k, nthreads=threads)
     dt = time.perf_counter() - t0
     # one host thread on the first 2^22 elements of the same sample, about 3 s
     n1 = min(n, 1 << 22)
@@ -246,7 +246,7 @@ def cpu_baseline(w, segs, S, target_s=12.0):
     reps1 = max(1, int(round(3.0 / pilot1)))
     t0 = time.perf_counter()
     for k in range(reps1):
-        oracle.shard_step(G1, *st1, hp, w.t_first + 1 + k, nthreads=1)
+        oracle.shard_step(G1, *st1, hp, w.t_first + 2 + k, nthreads=1)
     dt1 = time.perf_counter() - t0
     return {"value": n * reps / dt, "unit": "elem/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n} elements of the same shard (inputs generated untimed), "
@@ -718,7 +718,7 @@ def second_config(z, synth, name, args, stream):
           flush=True)
     del inp
     torch.cuda.empty_cache()
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, segs, S, target_s=8.0)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, segs, S, target_s=10.0)
     bpe = 2 * w.n_d + 26
     return {"workload": w.name, "description": WORKLOAD_LABEL[w.name], "shard_elems": S,
             "padded_elems": P, "n_d": w.n_d, "rank": w.rank, "buckets": L.n_buckets,
