@@ -626,8 +626,9 @@ int cu_count() {
 
 // Launch policy, from measurements on MI355X (Llama-3-8B and Llama-70B
 // shards, buffers placed by zero_placement_plan): one 256-thread block per
-// CU, except two 128-thread blocks per CU for fp32 contributions that are
-// not read-dominated (64 or more bytes of contributions per element); the
+// CU, except one 192-thread block per CU for bf16 contributions at N_d = 8
+// and two 128-thread blocks per CU for fp32 contributions that are not
+// read-dominated (64 or more bytes of contributions per element); the
 // cache policy and the chunk size below.
 constexpr bool read_dominated(int nd, int gt) { return nd * contrib_bytes(gt) >= 64; }
 // Cache policy, measured on the tuned llama8b / llama70b buffers (every
@@ -655,8 +656,16 @@ constexpr int step_group_max(int gt, int pairs) { return (fused(gt) || pairs > 1
 struct Policy {
   int blocks_per_cu, threads;
 };
+// bf16 contributions at N_d = 8 take one 192-thread block per CU (three
+// waves): measured against 256 threads on the tuned buffers, Llama-3-8B
+// 6.62-6.64 against 6.67-6.68 ms, 1.0 % or less faster at each of nine pool
+// starts; accum1p3b 1.075 against 1.087 ms; GPT-2 0.1068 against 0.1077 ms.
+// At N_d = 4, 16, 32 and 64 the same shape was 2-17 % slower, and with fp32
+// or accumulator contributions at N_d = 8 it was slower too (10.31 against
+// 9.67 ms, 13.63 against 12.23 ms), so they keep their shapes.
 Policy default_policy(int nd, int gt) {
   if (gt == GT_F32 && !read_dominated(nd, gt)) return Policy{2, 128};
+  if (gt == GT_BF16 && nd == 8) return Policy{1, 192};
   return Policy{1, 256};
 }
 
