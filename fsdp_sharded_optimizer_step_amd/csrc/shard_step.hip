@@ -626,10 +626,10 @@ int cu_count() {
 
 // Launch policy, from measurements on MI355X (Llama-3-8B and Llama-70B
 // shards, buffers placed by zero_placement_plan): one 256-thread block per
-// CU, except one 192-thread block per CU for bf16 contributions at N_d = 8
-// and two 128-thread blocks per CU for fp32 contributions that are not
-// read-dominated (64 or more bytes of contributions per element); the
-// cache policy and the chunk size below.
+// CU, except one 192-thread block per CU for the flat-addressed kernel over
+// bf16 contributions at N_d = 8 and two 128-thread blocks per CU for fp32
+// contributions that are not read-dominated (64 or more bytes of
+// contributions per element); the cache policy and the chunk size below.
 constexpr bool read_dominated(int nd, int gt) { return nd * contrib_bytes(gt) >= 64; }
 // Cache policy, measured on the tuned llama8b / llama70b buffers (every
 // policy and launch shape, N_d = 8 to 64): with each cache line fetched by a
@@ -656,16 +656,19 @@ constexpr int step_group_max(int gt, int pairs) { return (fused(gt) || pairs > 1
 struct Policy {
   int blocks_per_cu, threads;
 };
-// bf16 contributions at N_d = 8 take one 192-thread block per CU (three
-// waves): measured against 256 threads on the tuned buffers, Llama-3-8B
-// 6.62-6.64 against 6.67-6.68 ms, 1.0 % or less faster at each of nine pool
-// starts; accum1p3b 1.075 against 1.087 ms; GPT-2 0.1068 against 0.1077 ms.
-// At N_d = 4, 16, 32 and 64 the same shape was 2-17 % slower, and with fp32
-// or accumulator contributions at N_d = 8 it was slower too (10.31 against
-// 9.67 ms, 13.63 against 12.23 ms), so they keep their shapes.
-Policy default_policy(int nd, int gt) {
+// The vector kernel with flat addressing (All-Gather slot output or FLAT
+// contributions) over bf16 contributions at N_d = 8 takes one 192-thread
+// block per CU (three waves): measured against 256 threads on the tuned
+// buffers, Llama-3-8B 6.62-6.64 against 6.67-6.68 ms and faster at each of
+// nine pool starts (by 0.1-1.2 %); accum1p3b 1.075 against 1.087 ms; GPT-2
+// 0.1068 against 0.1077 ms.  Elsewhere three waves were slower: the same
+// kernel at N_d = 4, 16 and 32 (2-17 %), the in-place form without flat
+// addressing at N_d = 8 (the per-parameter Llama-3-8B shard, 7.41 against
+// 6.74 ms), the per-parameter table launches (6.86 against 6.63 ms), N_d =
+// 64 (1.7 %) and fp32 or accumulator contributions at N_d = 8.
+Policy default_policy(int nd, int gt, bool flat_vec) {
   if (gt == GT_F32 && !read_dominated(nd, gt)) return Policy{2, 128};
-  if (gt == GT_BF16 && nd == 8) return Policy{1, 192};
+  if (flat_vec && gt == GT_BF16 && nd == 8) return Policy{1, 192};
   return Policy{1, 256};
 }
 
@@ -869,7 +872,10 @@ int run_step(const zero_layout* L, const zero_adamw* hp, int64_t t, Call c, int3
   bool aligned = aligned16(c.master) && aligned16(c.m) && aligned16(c.v) && aligned16(c.pout) &&
                  (!c.gout || aligned16(c.gout));
   for (int q = 0; q < n_ins; ++q) aligned = aligned && aligned16(ins[q]);
-  const Policy pol = default_policy(nd, c.gt);
+  // the flat-addressed vector launches of a bucketed layout may take their
+  // own shape; table launches and the plain vector kernel take the default
+  const bool flat_vec = map && L->fixed();
+  const Policy pol = default_policy(nd, c.gt, flat_vec);
   const int threads = ls.threads > 0 ? ls.threads : pol.threads;
   const int cap = ls.blocks_cap > 0 ? ls.blocks_cap : cu_count() * pol.blocks_per_cu;
   const bool allow_vec = ls.path == 0 && aligned;
