@@ -327,9 +327,9 @@ int zero_shard_step_accumulate(const zero_layout* layout, const zero_adamw* hp, 
  * run concurrently on different streams.  Consecutive kernels of one stream
  * do not overlap, so one call per bucket pays each launch's ramp-up and
  * drain in turn: measured on MI355X for the Llama-3-8B shard (613 calls of
- * one 25 MiB bucket), 57 % of the HBM peak on one stream against 76-77 %
- * with the calls alternating between two streams (79 % for the whole shard
- * in one call).
+ * one 25 MiB bucket), 59 % of the HBM peak on one stream against 75 %
+ * with the calls alternating between two streams (79-80 % for the whole
+ * shard in one call or in calls of 32 buckets).
  *
  * All buffers are the full-size ones of zero_shard_step_ex (contributions of
  * S or P values, S-element state, S- or P-element output); only the slices
