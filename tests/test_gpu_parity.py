@@ -207,6 +207,11 @@ EDGE = [
     ([256 * 33 + 7], 0, 256, 255, "flat", "ag_slot"),       # largest rank count
     ([8], 0, 8, 5, "flat", "ag_slot"),                      # one element per rank
     ([3], 0, 8, 7, "flat", "ag_slot"),                      # this rank holds only padding
+    # N_d = 2: five vector buckets, then a last slot at an odd flat offset
+    ([2 * 4096 * 3 + 999, 77], 5000, 2, 1, "flat", "ag_slot"),
+    ([2 * 70000 + 1], 0, 2, 0, "compact", "shard"),         # 136 full chunks + 369 tail
+    # N_d = 32: slices of 1040, a 2-element last slice
+    ([32 * 1040 * 3 + 45], 32 * 1040, 32, 7, "compact", "ag_slot"),
 ]
 
 
@@ -828,6 +833,8 @@ F32_EDGE = [
     ([20000, 20001], 0, 16, 15, "compact", "shard"),
     ([64 * 300 + 1], 6400, 64, 63, "compact", "shard"),
     ([100 * 97], 0, 100, 99, "flat", "ag_slot"),
+    ([2 * 70000 + 1], 0, 2, 1, "flat", "ag_slot"),
+    ([32 * 1040 * 3 + 45], 32 * 1040, 32, 31, "flat", "ag_slot"),
 ]
 
 
@@ -968,6 +975,8 @@ FUSED_EDGE = [
     ([64 * 300 + 1], 6400, 64, 63, "compact", "shard"),
     ([100 * 97], 0, 100, 99, "flat", "ag_slot"),
     ([128 * 40 + 3], 0, 128, 127, "compact", "ag_slot"),
+    ([2 * 70000 + 1], 0, 2, 1, "flat", "ag_slot"),
+    ([32 * 1040 * 3 + 45], 32 * 1040, 32, 31, "compact", "shard"),
 ]
 
 
