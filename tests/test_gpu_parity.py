@@ -1090,6 +1090,8 @@ GATHER = [
     ([70000, 3], 16384, 8),       # vector path, short last bucket
     ([64 * 300 + 1], 6400, 64),
     ([256 * 33 + 7], 0, 256),
+    ([2 * 4096 * 3 + 999, 77], 5000, 2),
+    ([32 * 1040 * 3 + 45], 32 * 1040, 32),
 ]
 
 
