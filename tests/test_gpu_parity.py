@@ -121,6 +121,40 @@ def test_pack_cuts_pieces_longer_than_2_pow_30():
         torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(300)
+def test_pack_and_gather_split_into_several_launches():
+    """One tensor of 2^32 + 12349 elements at N_d = 4 (one bucket, 3 pad
+    elements): the pack needs 2^20 + 5 tiles of 4096 elements and the gather
+    2^21 + 8 items of 2048 elements, more blocks than one launch takes (the
+    dispatch grid counts work-items in 32 bits), so both are cut into several
+    launches.  Pack: the flat buffer is the tensor, then +0 padding; gather
+    of the flat buffer's four quarters (the rank shards): the flat buffer.
+    Values are random 16-bit patterns, so a misplaced block shows."""
+    n = (1 << 32) + 12349
+    L = z.Layout([n], 0, 4, 2)
+    P, S = L.padded, L.shard
+    assert (P, S) == (n + 3, (n + 3) // 4) and S % 8 == 0
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(20260)
+    src = torch.randint(-32768, 32768, (n,), dtype=torch.int16, device=DEV, generator=gen)
+    flat = torch.full((P,), CANARY, dtype=torch.int16, device=DEV)
+    say(f"  pack of {n} elements into {P}")
+    z.zero_bucket_pack(L, [src], flat)
+    torch.cuda.synchronize()
+    assert torch.equal(flat[:n], src), "packed tensor"
+    assert not flat[n:].any(), "bucket padding is +0"
+    del src
+    torch.cuda.empty_cache()
+    shards = [flat[q * S:(q + 1) * S].clone() for q in range(4)]
+    out = torch.full((P,), CANARY, dtype=torch.int16, device=DEV)
+    say(f"  gather of 4 shards of {S} elements")
+    z.zero_gather_params(L, shards, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, flat), "gathered flat buffer"
+    del shards, out, flat
+    torch.cuda.empty_cache()
+
+
 def test_gpt2s_ten_steps_full():
     case = Case(workloads.get("gpt2s"))
     run_steps(case, full_check_steps=(1,))
